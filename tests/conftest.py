@@ -1,0 +1,31 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def gpu_available() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def twn():
+    """The HIP binding.  GPU tests fail loudly (no fallback) if the library
+    is missing on a machine that has a GPU."""
+    if not gpu_available():
+        pytest.skip("no GPU visible")
+    import reduce_residual_add_amd as twn
+    twn.load()  # raises if libtwnorm.so is absent
+    return twn
