@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark: fused reduce of N partials + residual add + RMSNorm on one
+MI355X, reported as algorithmic HBM GB/s, fraction of the 8 TB/s peak and
+token-rows/s.
+
+Default workload: N=8 partials of [1024, 8192] bf16 (one 8-way shard of
+8192 tokens at a 70B-class hidden size).  A step is one fused call over one
+rotating set of resident buffers; S sets totalling at least twice the 256 MB
+Infinity Cache are cycled so the timed bytes come from HBM, not the cache.
+
+Prints ONE JSON line.  --report PATH also writes a detailed JSON (other
+workloads, the unfused pair, the plain-copy ceiling, the CU-limit sweep).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused reduce+RMSNorm HBM GB/s (% of peak) and token-rows/s at H=8192, N=8"
+PEAK_GBS = 8000.0              # MI355X HBM3E, published
+MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["reduce_residual_add_amd/csrc/twnorm_kernels.hpp",
+                  "reduce_residual_add_amd/csrc/twnorm_launch_impl.hpp",
+                  "reduce_residual_add_amd/csrc/twnorm_validate.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"fused_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default="shard70b")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cu", type=int, default=0, help="n_cu_limit of the timed calls (0 = whole chip)")
+    p.add_argument("--rotate", type=int, default=0, help="rotating buffer sets (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--report", default="", help="write a detailed JSON report here")
+    return p.parse_args(argv)
+
+
+# ---------------------------------------------------------------------------
+# device buffers
+# ---------------------------------------------------------------------------
+
+
+def _to_dev(arr, dtype):
+    import numpy as np
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def make_sets(inp, n_sets):
+    """n_sets resident copies of the inputs (+ outputs); set 0 holds the
+    host draw, the others are device clones at other addresses."""
+    import torch
+    dt = inp["dtype"]
+    base = dict(parts=[_to_dev(p, dt) for p in inp["partials"]], res=_to_dev(inp["residual"], dt),
+                w=_to_dev(inp["weight"], dt))
+    sets = []
+    for s in range(n_sets):
+        if s == 0:
+            d = dict(base)
+        else:
+            d = dict(parts=[p.clone() for p in base["parts"]], res=base["res"].clone(), w=base["w"].clone())
+        d["out"] = torch.empty_like(d["res"])
+        d["res_out"] = torch.empty_like(d["res"])
+        d["red"] = torch.empty_like(d["res"])
+        sets.append(d)
+    torch.cuda.synchronize()
+    return sets
+
+
+def n_rotating_sets(set_bytes, requested):
+    if requested > 0:
+        return requested
+    s = 3
+    while s * set_bytes < 2 * MALL_BYTES:
+        s += 1
+    return s
+
+
+def time_steps(step_fns, steps, warmup):
+    """Warm up, then time exactly `steps` calls between two events on the
+    current stream; returns (ms per step, wall seconds)."""
+    import torch
+    n = len(step_fns)
+    for i in range(warmup):
+        step_fns[i % n]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        step_fns[i % n]()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded row sample (the only use of oracle/)
+# ---------------------------------------------------------------------------
+
+
+def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
+    import numpy as np
+    from oracle import twnorm_oracle as O
+    rows_total = inp["rows"]
+    chunk = min(rows_total, 64)
+    done_rows = 0
+    spent = 0.0
+    first = None
+    start = 0
+    while spent < target_seconds and spent < 30.0:
+        sl = slice(start, start + chunk)
+        sub = dict(inp, partials=[p[sl] for p in inp["partials"]], residual=inp["residual"][sl])
+        t0 = time.perf_counter()
+        ref_out, ref_res = O.fused_from_storage(sub)
+        spent += time.perf_counter() - t0
+        if first is None:
+            first = (sl, ref_out, ref_res)
+        done_rows += chunk
+        start = (start + chunk) % rows_total
+        if start + chunk > rows_total:
+            start = 0
+    rows_per_s = done_rows / spent
+    bytes_per_row = (w.n + 3) * w.hidden * w.elem_bytes
+    # parity of the GPU's first rows against the oracle rows just computed
+    sl, ref_out, ref_res = first
+    got_out = O.decode(gpu_out[sl], w.dtype)
+    got_res = O.decode(gpu_res_out[sl], w.dtype)
+
+    def fails(got, ref):
+        d = np.abs(got - ref)
+        bound = (np.maximum(2e-2, 1e-2 * np.abs(ref)) if w.dtype == "bf16"
+                 else 1e-5 * np.maximum(1.0, np.abs(ref)))
+        return int(np.count_nonzero(~(d <= bound))), float(d.max())
+
+    f_out, m_out = fails(got_out, ref_out)
+    f_res, m_res = fails(got_res, ref_res)
+    return {
+        "value": round(rows_per_s * bytes_per_row / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle on {done_rows} token rows ({chunk}-row slices of the "
+                  f"same {w.name} inputs, {spent:.1f} s, single thread); "
+                  f"{rows_per_s:.1f} rows/s",
+        "rows_per_s": round(rows_per_s, 2),
+        "host_cpu": _cpu_model(),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "parity_rows": f"{sl.start}:{sl.stop}",
+        "parity_fails": f_out + f_res,
+        "parity_max_abs": max(m_out, m_res),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _from_dev(t, dtype):
+    import numpy as np
+    import torch
+    t = t.detach().cpu()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# ---------------------------------------------------------------------------
+# main measurement
+# ---------------------------------------------------------------------------
+
+
+def measure_fused(twn, w, sets, cu, steps, warmup):
+    fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"], n_cu_limit=cu)
+           for d in sets]
+    ms, wall = time_steps(fns, steps, warmup)
+    return ms, wall
+
+
+def measure_unfused(twn, w, sets, steps, warmup):
+    def pair(d):
+        def f():
+            twn.reduce(d["parts"], out=d["red"])
+            twn.rmsnorm(d["red"], d["res"], d["w"], w.eps, out=d["out"], residual_out=d["res_out"])
+        return f
+    return time_steps([pair(d) for d in sets], steps, warmup)
+
+
+def measure_copy(twn, total_bytes, steps, warmup):
+    import torch
+    n = total_bytes // 2
+    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(2)]
+    fns = [lambda a=a, b=b: twn.stream_copy(a, b) for a, b in bufs]
+    ms, _ = time_steps(fns, steps, warmup)
+    return ms, n
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU "
+                                   "path is a design only (see DESIGN.md)", "n_gpus": args.gpus}))
+        return 2
+    import torch
+    import reduce_residual_add_amd as twn
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    twn.load()
+    w = workloads.get(args.workload)
+    inp = workloads.make(w, seed=args.seed)
+    set_bytes = w.fused_bytes() + w.rows * w.hidden * w.elem_bytes   # + the unfused intermediate
+    n_sets = n_rotating_sets(set_bytes, args.rotate)
+    sets = make_sets(inp, n_sets)
+
+    ms, wall = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup)
+    bytes_call = w.fused_bytes()
+    gbs = bytes_call / (ms * 1e-3) / 1e9
+    rows_per_s = w.rows / (ms * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_partials": w.n, "rows": w.rows, "hidden": w.hidden,
+                   "dtype": w.dtype, "eps": w.eps, "n_cu_limit": args.cu,
+                   "rotating_sets": n_sets, "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+        "token_rows_per_s": round(rows_per_s, 1),
+        "algorithmic_bytes_per_step": bytes_call,
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_GBS, 4), "traffic": counter_traffic(w.name)},
+    }
+
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        d0 = sets[0]
+        # recompute set 0 once so its outputs are the ones checked
+        twn.fused_reduce_rmsnorm(d0["parts"], d0["res"], d0["w"], w.eps, out=d0["out"],
+                                 residual_out=d0["res_out"])
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(inp, w, _from_dev(d0["out"], w.dtype),
+                                              _from_dev(d0["res_out"], w.dtype), args.cpu_seconds)
+
+    if args.report:
+        rep = {"main": result, "kernel_source_sha256": kernel_source_hash()}
+        ums, _ = measure_unfused(twn, w, sets, max(50, args.steps // 4), 10)
+        rep["unfused_pair"] = {"ms_per_step": ums, "algorithmic_bytes": w.unfused_bytes(),
+                               "gbs_on_unfused_bytes": w.unfused_bytes() / (ums * 1e-3) / 1e9,
+                               "speedup_fused_vs_unfused": ums / ms}
+        cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
+        rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes,
+                               "gbs": 2 * cbytes / (cms * 1e-3) / 1e9}
+        # cache-resident figure (one buffer set, repeated): NOT an HBM number
+        wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
+        rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
+        with open(args.report, "w") as f:
+            json.dump(rep, f, indent=1)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

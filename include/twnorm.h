@@ -1,0 +1,161 @@
+/*
+ * twnorm.h -- C ABI of libtwnorm: fused "reduce N tensor-parallel partial
+ * outputs + residual add + RMSNorm * weight" for one GPU's token-sharded rows,
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [TW] "TokenWeave 策略详解：以大模型推理为例" (nanhubrain.csdn.net)
+ *   [TP] "张量并行Tensor Parallelism" (scmmm.top)
+ *
+ * What is computed, per token row t and feature j (float32 arithmetic):
+ *   s[t,j]            = p_0[t,j] + p_1[t,j] + ... + p_{n-1}[t,j]   (index order)
+ *   x[t,j]            = residual[t,j] + s[t,j]
+ *   residual_out[t,j] = round(x[t,j])
+ *   out[t,j]          = round(x[t,j] * rsqrt(mean_j' x[t,j']^2 + eps) * weight[j])
+ * where the mean runs over all `hidden` features of the token and round() is
+ * round-to-nearest-even into the storage type.  The sum of partials is the
+ * per-shard half of a token-boundary ReduceScatter ([TW] §2, §3.2; the
+ * appendix's zero-padded column partials, and [TP] MLP: Y = sum_i Y_i); the
+ * add + norm is [TW] §1's  output = RMSNorm(residual + allreduce_output) *
+ * weight, run on this shard's rows only ([TW] §3.3); the new residual is the
+ * X = X + Y update of [TP] Self-Attention, fused in registers as in [TW] §5.
+ *
+ * Common conventions (every entry point):
+ *   Layout     Each of partials[i], residual, out, residual_out, reduced is a
+ *              row-major contiguous [rows, hidden] array of `dtype`; weight is
+ *              [hidden] of `dtype`.  A token shard is a row range, so callers
+ *              pass pointers already offset to the shard's first row.
+ *   Memory     All data pointers are device pointers owned by the caller.  The
+ *              library never allocates, frees or keeps them after returning.
+ *              The host array `partials` is read during the call only.
+ *   Execution  Asynchronous: work is enqueued on `stream` (a hipStream_t
+ *              passed as an opaque pointer; NULL = the null stream) and the
+ *              call returns.  No device synchronisation, no allocation.
+ *   Errors     Arguments are validated first, without any HIP call; on an
+ *              error nothing is enqueued and nothing is written.
+ *                TW_ERR_INVALID_ARG  null pointer, n outside [1, 16], rows < 0,
+ *                                    hidden < 1, eps negative / NaN / Inf,
+ *                                    n_cu_limit < 0, unknown dtype, or
+ *                                    rows * hidden too large for 64-bit bytes.
+ *                TW_ERR_UNSUPPORTED  hidden * sizeof(dtype) not a multiple of
+ *                                    16, a pointer not 16-byte aligned, or
+ *                                    hidden beyond TW_MAX_HIDDEN_BYTES bytes.
+ *                TW_ERR_ALIAS        an output overlaps an input it may not
+ *                                    (rules per entry point below).
+ *                TW_ERR_HIP          a HIP runtime call or the launch failed;
+ *                                    tw_last_error() has the HIP message.
+ *              rows == 0 is a no-op returning TW_OK (after validation).
+ *              Faults inside a kernel surface at the caller's next
+ *              synchronisation, as for any HIP launch.
+ *   n_cu_limit 0, or any value >= the device's CU count, uses the whole chip.
+ *              k in [1, CUs) runs the kernel on at most k CUs (persistent grid
+ *              on a cached CU-masked stream, ordered after and before `stream`
+ *              by events).  Results are bit-identical for every n_cu_limit.
+ *   Determinism The summation order depends only on (dtype, hidden, n): the
+ *              same row gives the same bits whatever rows, shard offset or
+ *              n_cu_limit are.
+ *   Threads    Entry points may be called from several host threads; the
+ *              per-device cache (CU count, masked streams) is mutex-guarded.
+ */
+#ifndef TWNORM_H
+#define TWNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TW_OK = 0,
+  TW_ERR_INVALID_ARG = -1,
+  TW_ERR_UNSUPPORTED = -2,
+  TW_ERR_ALIAS = -3,
+  TW_ERR_HIP = -4
+} tw_status;
+
+typedef enum { TW_BF16 = 0, TW_F32 = 1 } tw_dtype;
+
+#define TW_ABI_VERSION 1
+#define TW_MAX_PARTIALS 16
+/* Largest supported row: 16 waves x 64 lanes x 8 chunks of 16 bytes. */
+#define TW_MAX_HIDDEN_BYTES (16 * 64 * 8 * 16)
+
+/*
+ * Fused path: out = RMSNorm(residual + sum_i partials[i]) * weight and
+ * residual_out = residual + sum_i partials[i], in one pass over HBM.
+ *   partials      host array of n device pointers, each [rows, hidden]
+ *   n             number of partials, 1..TW_MAX_PARTIALS
+ *   rows, hidden  shard size in token rows and features per token
+ *   dtype         storage type of every tensor (arithmetic is float32)
+ *   residual      [rows, hidden] input
+ *   weight        [hidden]
+ *   eps           added to the mean square inside the square root, >= 0
+ *   out           [rows, hidden] normalised output
+ *   residual_out  [rows, hidden] updated residual; may be exactly `residual`
+ *                 (in-place update) but may not overlap it partially
+ *   n_cu_limit, stream   see above
+ * Alias rules: out may not overlap any input or residual_out; residual_out
+ * may not overlap a partial or weight, nor residual except by equality.
+ */
+tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int n, int64_t rows,
+                                  int64_t hidden, tw_dtype dtype, const void* residual,
+                                  const void* weight, float eps, void* out,
+                                  void* residual_out, int n_cu_limit, void* stream);
+
+/*
+ * Unfused comparison path, first half: reduced = round(sum_i partials[i]),
+ * the reduce of a ReduceScatter written to HBM ([TW] §4: the intermediate
+ * makes a round trip through HBM).  `reduced` may be exactly one of the
+ * partials (in place) but may not overlap any partially.
+ */
+tw_status tw_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                    tw_dtype dtype, void* reduced, int n_cu_limit, void* stream);
+
+/*
+ * Unfused comparison path, second half: residual_out = residual + reduced and
+ * out = RMSNorm(residual_out) * weight ([TW] §1 formula, §3.3), reading the
+ * reduced tensor back from HBM.  Same alias rules as the fused path with
+ * `reduced` in the place of the partials.  Identical in results to
+ * tw_fused_reduce_rmsnorm with n = 1 and partials = {reduced}.
+ */
+tw_status tw_rmsnorm(const void* reduced, int64_t rows, int64_t hidden, tw_dtype dtype,
+                     const void* residual, const void* weight, float eps, void* out,
+                     void* residual_out, int n_cu_limit, void* stream);
+
+/*
+ * Measurement aid (not part of the method): dst = src, `bytes` bytes, a
+ * plain 16-byte-vector streaming copy used as the practical HBM ceiling and
+ * to scale hardware traffic counters.  bytes must be a multiple of 16 and both
+ * pointers 16-byte aligned; the ranges may not overlap.
+ */
+tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit,
+                         void* stream);
+
+/*
+ * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts
+ * per token row with `chunks_per_lane` 16-byte chunks per lane (both 0 =
+ * automatic choice).  Applies to every later call on every thread; a shape
+ * that cannot cover a row returns TW_ERR_UNSUPPORTED at the call.  Changing
+ * the shape may change the last bit of results (a different reduction tree).
+ * Returns TW_ERR_INVALID_ARG for waves outside [0,16] or chunks_per_lane not
+ * in {0,1,2,3,4,6,8}.
+ */
+tw_status tw_set_fused_shape(int waves, int chunks_per_lane);
+
+/* Launch shape the fused kernel would use for (dtype, hidden); writes the
+ * wavefronts per row and chunks per lane (team_lanes for rows narrower than
+ * one wavefront, else 0).  HIP-free. */
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int* waves,
+                               int* chunks_per_lane, int* team_lanes);
+
+const char* tw_status_string(tw_status s);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* tw_last_error(void);
+int tw_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWNORM_H */

@@ -1,0 +1,267 @@
+"""Python binding of libtwnorm: fused reduce of N tensor-parallel partials +
+residual add + RMSNorm * weight on one MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libtwnorm.so`` (built in-tree by ``reduce_residual_add_amd.build``).
+PyTorch provides device memory and the current HIP stream.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+The C entry points are declared in ``include/twnorm.h``; the functions below
+carry the same names without the ``tw_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libtwnorm.so")
+
+TW_OK, TW_ERR_INVALID_ARG, TW_ERR_UNSUPPORTED, TW_ERR_ALIAS, TW_ERR_HIP = 0, -1, -2, -3, -4
+TW_BF16, TW_F32 = 0, 1
+TW_MAX_PARTIALS = 16
+TW_ABI_VERSION = 1
+
+_lib: Optional[ctypes.CDLL] = None
+
+_c = ctypes
+_vp = _c.c_void_p
+_i64 = _c.c_int64
+
+
+class TwError(RuntimeError):
+    """A non-OK status from libtwnorm."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
+                 TW_ERR_UNSUPPORTED: "TW_ERR_UNSUPPORTED", TW_ERR_ALIAS: "TW_ERR_ALIAS",
+                 TW_ERR_HIP: "TW_ERR_HIP"}
+
+EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_reduce", "tw_rmsnorm", "tw_stream_copy",
+            "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
+            "tw_last_error", "tw_abi_version")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libtwnorm.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m reduce_residual_add_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    lib.tw_fused_reduce_rmsnorm.argtypes = [_c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp,
+                                            _vp, _c.c_float, _vp, _vp, _c.c_int, _vp]
+    lib.tw_fused_reduce_rmsnorm.restype = _c.c_int
+    lib.tw_reduce.argtypes = [_c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp, _c.c_int, _vp]
+    lib.tw_reduce.restype = _c.c_int
+    lib.tw_rmsnorm.argtypes = [_vp, _i64, _i64, _c.c_int, _vp, _vp, _c.c_float, _vp, _vp,
+                               _c.c_int, _vp]
+    lib.tw_rmsnorm.restype = _c.c_int
+    lib.tw_stream_copy.argtypes = [_vp, _vp, _i64, _c.c_int, _vp]
+    lib.tw_stream_copy.restype = _c.c_int
+    lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int]
+    lib.tw_set_fused_shape.restype = _c.c_int
+    lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.POINTER(_c.c_int),
+                                         _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]
+    lib.tw_query_fused_shape.restype = _c.c_int
+    lib.tw_status_string.argtypes = [_c.c_int]
+    lib.tw_status_string.restype = _c.c_char_p
+    lib.tw_last_error.argtypes = []
+    lib.tw_last_error.restype = _c.c_char_p
+    lib.tw_abi_version.argtypes = []
+    lib.tw_abi_version.restype = _c.c_int
+    if lib.tw_abi_version() != TW_ABI_VERSION:
+        raise ImportError(f"libtwnorm ABI {lib.tw_abi_version()} != {TW_ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().tw_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != TW_OK:
+        raise TwError(status, last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch plumbing (device memory, dtype tag, current stream)
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TW_BF16
+    if t.dtype == torch.float32:
+        return TW_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _check_tensor(t, name: str, shape, dt, device) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dt:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dt}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _rows_hidden(t):
+    if t.dim() != 2:
+        raise ValueError("tensors are [rows, hidden]")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+
+
+def fused_reduce_rmsnorm(partials: Sequence, residual, weight, eps: float, *, out=None,
+                         residual_out=None, n_cu_limit: int = 0, stream=None):
+    """out = RMSNorm(residual + sum(partials)) * weight; residual_out =
+    residual + sum(partials).  Pass ``residual_out=residual`` for the in-place
+    residual update.  Returns (out, residual_out)."""
+    torch = _torch()
+    lib = load()
+    rows, hidden = _rows_hidden(residual)
+    dt, dev = residual.dtype, residual.device
+    n = len(partials)
+    if n < 1 or n > TW_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TW_MAX_PARTIALS} partials, got {n}")
+    for i, p in enumerate(partials):
+        _check_tensor(p, f"partials[{i}]", (rows, hidden), dt, dev)
+    _check_tensor(residual, "residual", (rows, hidden), dt, dev)
+    _check_tensor(weight, "weight", (hidden,), dt, dev)
+    if out is None:
+        out = torch.empty_like(residual)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _check_tensor(out, "out", (rows, hidden), dt, dev)
+    _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    if rows == 0:   # nothing to do (an empty tensor's data_ptr() may be NULL)
+        return out, residual_out
+    arr = (_vp * n)(*[p.data_ptr() for p in partials])
+    _check(lib.tw_fused_reduce_rmsnorm(arr, n, rows, hidden, dtype_code(residual),
+                                       residual.data_ptr(), weight.data_ptr(), float(eps),
+                                       out.data_ptr(), residual_out.data_ptr(), int(n_cu_limit),
+                                       _stream_ptr(stream)))
+    return out, residual_out
+
+
+def reduce(partials: Sequence, *, out=None, n_cu_limit: int = 0, stream=None):
+    """reduced = sum(partials), rounded to the storage dtype (the unfused
+    path's HBM intermediate).  Returns ``reduced``."""
+    torch = _torch()
+    lib = load()
+    n = len(partials)
+    if n < 1 or n > TW_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TW_MAX_PARTIALS} partials, got {n}")
+    rows, hidden = _rows_hidden(partials[0])
+    dt, dev = partials[0].dtype, partials[0].device
+    for i, p in enumerate(partials):
+        _check_tensor(p, f"partials[{i}]", (rows, hidden), dt, dev)
+    if out is None:
+        out = torch.empty_like(partials[0])
+    _check_tensor(out, "out", (rows, hidden), dt, dev)
+    if rows == 0:
+        return out
+    arr = (_vp * n)(*[p.data_ptr() for p in partials])
+    _check(lib.tw_reduce(arr, n, rows, hidden, dtype_code(out), out.data_ptr(), int(n_cu_limit),
+                         _stream_ptr(stream)))
+    return out
+
+
+def rmsnorm(reduced, residual, weight, eps: float, *, out=None, residual_out=None,
+            n_cu_limit: int = 0, stream=None):
+    """out = RMSNorm(residual + reduced) * weight; residual_out = residual +
+    reduced.  The unfused path's second kernel.  Returns (out, residual_out)."""
+    torch = _torch()
+    lib = load()
+    rows, hidden = _rows_hidden(residual)
+    dt, dev = residual.dtype, residual.device
+    _check_tensor(reduced, "reduced", (rows, hidden), dt, dev)
+    _check_tensor(residual, "residual", (rows, hidden), dt, dev)
+    _check_tensor(weight, "weight", (hidden,), dt, dev)
+    if out is None:
+        out = torch.empty_like(residual)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _check_tensor(out, "out", (rows, hidden), dt, dev)
+    _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    if rows == 0:
+        return out, residual_out
+    _check(lib.tw_rmsnorm(reduced.data_ptr(), rows, hidden, dtype_code(residual),
+                          residual.data_ptr(), weight.data_ptr(), float(eps), out.data_ptr(),
+                          residual_out.data_ptr(), int(n_cu_limit), _stream_ptr(stream)))
+    return out, residual_out
+
+
+def stream_copy(src, dst, *, n_cu_limit: int = 0, stream=None):
+    """dst = src byte for byte (measurement aid: the plain-copy ceiling)."""
+    lib = load()
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst sizes differ")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    _check(lib.tw_stream_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
+                              int(n_cu_limit), _stream_ptr(stream)))
+    return dst
+
+
+def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0) -> None:
+    """Force the fused kernel's launch shape (0, 0 = automatic)."""
+    _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane)))
+
+
+def query_fused_shape(dtype: int, hidden: int):
+    """(waves, chunks_per_lane, team_lanes) the fused kernel uses."""
+    w, k, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().tw_query_fused_shape(int(dtype), int(hidden), ctypes.byref(w), ctypes.byref(k),
+                                       ctypes.byref(t)))
+    return w.value, k.value, t.value
+
+
+class PreparedFused:
+    """Pre-marshalled arguments of one fused call, for tight timing loops:
+    ``__call__`` is one ctypes call with no per-call conversions."""
+
+    def __init__(self, partials, residual, weight, eps, out, residual_out, n_cu_limit=0,
+                 stream=None):
+        self._lib = load()
+        self._keep = (list(partials), residual, weight, out, residual_out)
+        self._n = len(partials)
+        self._arr = (_vp * self._n)(*[p.data_ptr() for p in partials])
+        rows, hidden = _rows_hidden(residual)
+        self._args = (self._arr, self._n, rows, hidden, dtype_code(residual), residual.data_ptr(),
+                      weight.data_ptr(), ctypes.c_float(float(eps)), out.data_ptr(),
+                      residual_out.data_ptr(), int(n_cu_limit), _stream_ptr(stream))
+
+    def __call__(self) -> None:
+        st = self._lib.tw_fused_reduce_rmsnorm(*self._args)
+        if st != TW_OK:
+            _check(st)

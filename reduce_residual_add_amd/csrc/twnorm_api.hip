@@ -1,0 +1,188 @@
+// C-ABI entry points of libtwnorm (declared in include/twnorm.h).
+//
+// Each entry point validates its arguments without touching HIP
+// (twnorm_validate.cpp), picks the launch shape from (dtype, hidden) only, and
+// enqueues one kernel on the caller's stream -- or, for a CU limit, on a
+// cached CU-masked stream that is ordered after the caller's stream and
+// before its later work by a pair of events.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "twnorm.h"
+#include "twnorm_launch.hpp"
+#include "twnorm_validate.hpp"
+
+namespace {
+
+struct DeviceState {
+  int cus = 0;
+  std::map<int, hipStream_t> masked;  // n_cu_limit -> CU-masked stream
+  hipEvent_t ev_in = nullptr;
+  hipEvent_t ev_out = nullptr;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_dev;
+
+tw_status hip_fail(hipError_t e, const char* what) {
+  return twv::fail(TW_ERR_HIP, "%s: %s (hipError %d)", what, hipGetErrorString(e),
+                   static_cast<int>(e));
+}
+
+// Per-device cache entry for the current device.  Caller holds g_mu.
+tw_status device_state(DeviceState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  DeviceState& d = g_dev[dev];
+  if (d.cus == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+    if (cus < 1) return twv::fail(TW_ERR_HIP, "device reports %d CUs", cus);
+    d.cus = cus;
+  }
+  if (d.ev_in == nullptr) {
+    e = hipEventCreateWithFlags(&d.ev_in, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+    e = hipEventCreateWithFlags(&d.ev_out, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  *out = &d;
+  return TW_OK;
+}
+
+// A stream whose kernels may only occupy the CUs of the first `k` mask bits.
+// Streams keep the default priority.  Caller holds g_mu.
+tw_status masked_stream(DeviceState& d, int k, hipStream_t* out) {
+  auto it = d.masked.find(k);
+  if (it != d.masked.end()) {
+    *out = it->second;
+    return TW_OK;
+  }
+  std::vector<uint32_t> mask((d.cus + 31) / 32, 0u);
+  for (int i = 0; i < k; ++i) mask[i / 32] |= 1u << (i % 32);
+  hipStream_t s = nullptr;
+  hipError_t e = hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data());
+  if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask");
+  d.masked[k] = s;
+  *out = s;
+  return TW_OK;
+}
+
+// Run `launch(cu_limit, stream)` on the whole chip or on a CU-limited stream.
+template <typename F>
+tw_status run(int n_cu_limit, hipStream_t caller, const char* what, F&& launch) {
+  if (n_cu_limit == 0) {
+    hipError_t e = launch(0, caller);
+    return e == hipSuccess ? TW_OK : hip_fail(e, what);
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* d = nullptr;
+  tw_status st = device_state(&d);
+  if (st != TW_OK) return st;
+  if (n_cu_limit >= d->cus) {
+    hipError_t e = launch(0, caller);
+    return e == hipSuccess ? TW_OK : hip_fail(e, what);
+  }
+  hipStream_t ms = nullptr;
+  st = masked_stream(*d, n_cu_limit, &ms);
+  if (st != TW_OK) return st;
+  hipError_t e = hipEventRecord(d->ev_in, caller);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = hipStreamWaitEvent(ms, d->ev_in, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  const hipError_t le = launch(n_cu_limit, ms);
+  e = hipEventRecord(d->ev_out, ms);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = hipStreamWaitEvent(caller, d->ev_out, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  return le == hipSuccess ? TW_OK : hip_fail(le, what);
+}
+
+tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                     tw_dtype dtype, const void* residual, const void* weight, float eps,
+                     void* out, void* residual_out, int n_cu_limit, void* stream) {
+  tw_status st = twv::check_fused(partials, n, rows, hidden, dtype, residual, weight, eps, out,
+                                  residual_out, n_cu_limit);
+  if (st != TW_OK) return st;
+  if (rows == 0) return TW_OK;
+  twv::Shape sh{};
+  st = twv::choose_shape(dtype, hidden, &sh);
+  if (st != TW_OK) return st;
+
+  twl::FusedArgs a{};
+  for (int i = 0; i < n; ++i) a.pp.p[i] = static_cast<const twk::u32x4*>(partials[i]);
+  a.residual = static_cast<const twk::u32x4*>(residual);
+  a.weight = static_cast<const twk::u32x4*>(weight);
+  a.out = static_cast<twk::u32x4*>(out);
+  a.residual_out = static_cast<twk::u32x4*>(residual_out);
+  a.rows = rows;
+  a.chunks = static_cast<int>(hidden * twv::elem_bytes(dtype) / 16);
+  a.hidden_f = static_cast<float>(hidden);
+  a.eps = eps;
+  twl::Launch L{n, sh.waves, sh.k, sh.team, 0};
+  return run(n_cu_limit, static_cast<hipStream_t>(stream), "fused kernel launch",
+             [&](int cu, hipStream_t s) {
+               L.cu_limit = cu;
+               return dtype == TW_BF16 ? twl::launch_fused_bf16(L, a, s)
+                                       : twl::launch_fused_f32(L, a, s);
+             });
+}
+
+}  // namespace
+
+extern "C" {
+
+tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int n, int64_t rows,
+                                  int64_t hidden, tw_dtype dtype, const void* residual,
+                                  const void* weight, float eps, void* out, void* residual_out,
+                                  int n_cu_limit, void* stream) {
+  twv::clear_error();
+  return fused_impl(partials, n, rows, hidden, dtype, residual, weight, eps, out, residual_out,
+                    n_cu_limit, stream);
+}
+
+tw_status tw_rmsnorm(const void* reduced, int64_t rows, int64_t hidden, tw_dtype dtype,
+                     const void* residual, const void* weight, float eps, void* out,
+                     void* residual_out, int n_cu_limit, void* stream) {
+  twv::clear_error();
+  const void* parts[1] = {reduced};
+  return fused_impl(parts, 1, rows, hidden, dtype, residual, weight, eps, out, residual_out,
+                    n_cu_limit, stream);
+}
+
+tw_status tw_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                    tw_dtype dtype, void* reduced, int n_cu_limit, void* stream) {
+  twv::clear_error();
+  tw_status st = twv::check_reduce(partials, n, rows, hidden, dtype, reduced, n_cu_limit);
+  if (st != TW_OK) return st;
+  if (rows == 0) return TW_OK;
+  twk::PartialPtrs pp{};
+  for (int i = 0; i < n; ++i) pp.p[i] = static_cast<const twk::u32x4*>(partials[i]);
+  const int64_t total = rows * (hidden * twv::elem_bytes(dtype) / 16);
+  auto* red = static_cast<twk::u32x4*>(reduced);
+  return run(n_cu_limit, static_cast<hipStream_t>(stream), "reduce kernel launch",
+             [&](int cu, hipStream_t s) {
+               return dtype == TW_BF16 ? twl::launch_reduce_bf16(n, pp, red, total, cu, s)
+                                       : twl::launch_reduce_f32(n, pp, red, total, cu, s);
+             });
+}
+
+tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit, void* stream) {
+  twv::clear_error();
+  tw_status st = twv::check_copy(src, dst, bytes, n_cu_limit);
+  if (st != TW_OK) return st;
+  if (bytes == 0) return TW_OK;
+  return run(n_cu_limit, static_cast<hipStream_t>(stream), "copy kernel launch",
+             [&](int cu, hipStream_t s) {
+               return twl::launch_copy(static_cast<const twk::u32x4*>(src),
+                                       static_cast<twk::u32x4*>(dst), bytes / 16, cu, s);
+             });
+}
+
+}  // extern "C"

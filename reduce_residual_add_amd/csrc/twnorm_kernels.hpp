@@ -1,0 +1,321 @@
+// Device code of libtwnorm for gfx950 (CDNA4, wave64).
+//
+// One token row is one independent unit of work: its statistic needs all of
+// its `hidden` features and nothing from other rows ("TokenWeave 策略详解：以
+// 大模型推理为例", §1: the per-token RMS uses all of a token's features; §2:
+// the ReduceScatter must cut along token boundaries for that reason).  So a
+// row is owned by one team of lanes and never leaves registers between its
+// loads and its stores:
+//
+//   loads   N partial chunks + 1 residual chunk per 16-byte chunk slot,
+//           all issued before the first add (memory-level parallelism)
+//   sum     s = p_0 + ... + p_{N-1} in index order, x = r + s   (float32)
+//   store   residual_out = round(x)            (the X = X + Y update)
+//   reduce  sum of x^2: per lane -> DPP / ds_swizzle butterfly inside the
+//           wavefront -> LDS across the wavefronts of the row
+//   store   out = round(x * rsqrt(ss / H + eps) * w)
+//
+// The pages' kernel sums the N peers inside the switch fabric with 16-byte
+// multimem loads ("融合内核中的体现": multimem_ld_reduce_add<16>); here the N
+// partials are local HBM buffers, read with N plain 16-byte loads and summed
+// in VGPRs, which is what a 16-byte-per-lane vector load does best on CDNA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twk {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxPartials = 16;
+constexpr int kMaxWaves = 16;  // wavefronts per row, wide-row kernel
+
+struct PartialPtrs {
+  const u32x4* p[kMaxPartials];
+};
+
+// Storage formats.  A 16-byte chunk holds kElems values.
+struct Bf16 {
+  static constexpr int kElems = 8;
+};
+struct F32 {
+  static constexpr int kElems = 4;
+};
+
+// ---------------------------------------------------------------------------
+// Streaming memory access.  Partials, residual and outputs are touched once
+// per call; TW_NT_LOADS / TW_NT_STORES select non-temporal hints for them.
+// ---------------------------------------------------------------------------
+#ifndef TW_NT_LOADS
+#define TW_NT_LOADS 0
+#endif
+#ifndef TW_NT_STORES
+#define TW_NT_STORES 0
+#endif
+
+__device__ __forceinline__ u32x4 ld_stream(const u32x4* p) {
+#if TW_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) {
+#if TW_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Format conversion.  bf16 -> f32 is exact (the bf16 bits are the high half
+// of a float32).  f32 -> bf16 uses v_cvt_pk_bf16_f32: round to nearest even,
+// NaN stays NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void widen(Bf16, const u32x4& v, float* f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = __uint_as_float(v[q] << 16);
+    f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void widen(F32, const u32x4& v, float* f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(v[q]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 narrow(Bf16, const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = pack_bf16x2(f[2 * q], f[2 * q + 1]);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 narrow(F32, const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = __float_as_uint(f[q]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums.  Butterfly over aligned lane groups: quad_perm swaps for
+// distance 1 and 2, row_half_mirror / row_mirror for 4 and 8 (earlier steps
+// made each 4- / 8-lane block uniform, so a mirror acts as a swap),
+// ds_swizzle xor 16 inside each 32-lane half, and the two halves' readlane
+// values for 32.  Every lane of a group ends with the same bits, and the
+// order of additions depends only on the group size.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+  // bit-mode swizzle: and_mask 0x1f, or_mask 0, xor_mask 0x10
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of `team` lanes (a power of two, 1..64).  `team`
+// must be uniform across the wavefront and every lane must be active.
+__device__ __forceinline__ float team_sum(float v, int team) {
+  if (team >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  if (team >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  if (team >= 8) v += dpp<0x141>(v);   // row_half_mirror
+  if (team >= 16) v += dpp<0x140>(v);  // row_mirror
+  if (team >= 32) v += swizzle_xor16(v);
+  if (team >= 64) v = readlane(v, 0) + readlane(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk arithmetic shared by both kernel shapes.
+// raw[0] is the residual chunk, raw[1..N] the partial chunks.
+// ---------------------------------------------------------------------------
+template <class D, int N>
+__device__ __forceinline__ void add_chunk(const u32x4 (&raw)[N + 1], float* x, float& ss) {
+  constexpr int E = D::kElems;
+  float acc[E], t[E];
+  widen(D{}, raw[1], acc);
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    widen(D{}, raw[i + 1], t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += t[e];
+  }
+  widen(D{}, raw[0], t);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = t[e] + acc[e];
+    ss = __builtin_fmaf(x[e], x[e], ss);
+  }
+}
+
+template <class D>
+__device__ __forceinline__ u32x4 scale_chunk(const float* x, float inv, const u32x4& wraw) {
+  constexpr int E = D::kElems;
+  float w[E], o[E];
+  widen(D{}, wraw, w);
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = (x[e] * inv) * w[e];
+  return narrow(D{}, o);
+}
+
+// ---------------------------------------------------------------------------
+// Wide rows: one workgroup of W wavefronts (blockDim.x = 64 W <= 64 MAXW) per
+// row, each lane owning K chunk slots c = tid + k * blockDim.x.  A slot's N+1
+// loads are issued together; its sum is kept in float32 registers (K * E
+// VGPRs) until the row's statistic is known.  Rows are visited with a grid
+// stride, so a grid smaller than `rows` (CU-limited mode) stays persistent.
+// MAXW sets the launch bound: 4 (256 threads) leaves the compiler up to 512
+// VGPRs per lane, 16 (1024 threads) caps it at 128.
+// ---------------------------------------------------------------------------
+template <class D, int N, int K, int MAXW>
+__global__ void __launch_bounds__(64 * MAXW)
+fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
+                  const u32x4* __restrict__ weight, u32x4* __restrict__ out,
+                  u32x4* residual_out, int64_t rows, int chunks, float hidden_f, float eps) {
+  constexpr int E = D::kElems;
+  __shared__ float red[2][MAXW];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+
+  u32x4 wv[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int c = tid + k * nthr;
+    if (c < chunks) wv[k] = weight[c];
+  }
+
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    // Row base pointers are wavefront-uniform (scalar registers); lanes add
+    // a 32-bit chunk offset, so loads and stores use the saddr + voffset form.
+    const int64_t base = row * chunks;
+    const u32x4* r_row = residual + base;
+    u32x4* ro_row = residual_out + base;
+    u32x4* o_row = out + base;
+    const u32x4* p_row[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) p_row[i] = pp.p[i] + base;
+    float x[K][E];
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const unsigned c = unsigned(tid + k * nthr);
+      if (c < unsigned(chunks)) {
+        u32x4 raw[N + 1];
+        raw[0] = ld_stream(r_row + c);
+#pragma unroll
+        for (int i = 0; i < N; ++i) raw[i + 1] = ld_stream(p_row[i] + c);
+        add_chunk<D, N>(raw, x[k], ss);
+        st_stream(ro_row + c, narrow(D{}, x[k]));
+      }
+    }
+    ss = team_sum(ss, 64);
+    if (MAXW > 1 && nwaves > 1) {
+      if ((tid & 63) == 0) red[parity][wave] = ss;
+      __syncthreads();
+      ss = 0.0f;
+      for (int w = 0; w < nwaves; ++w) ss += red[parity][w];
+      // Double-buffered slot: the next row writes the other half, and the
+      // row after that is only reached once every wave passed the next
+      // barrier, i.e. finished reading this half.
+      parity ^= 1;
+    }
+    const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const unsigned c = unsigned(tid + k * nthr);
+      if (c < unsigned(chunks)) st_stream(o_row + c, scale_chunk<D>(x[k], inv, wv[k]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Narrow rows (at most 32 chunks): a team of `team` lanes (power of two) per
+// row, 256 / team rows per 256-thread workgroup, one chunk per lane.  The
+// loop bound depends on blockIdx only, so whole wavefronts iterate together
+// and the butterfly always sees every lane active.
+// ---------------------------------------------------------------------------
+template <class D, int N>
+__global__ void __launch_bounds__(256)
+fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
+                  const u32x4* __restrict__ weight, u32x4* __restrict__ out,
+                  u32x4* residual_out, int64_t rows, int chunks, int team, float hidden_f,
+                  float eps) {
+  constexpr int E = D::kElems;
+  const int tid = threadIdx.x;
+  const int rows_per_block = blockDim.x / team;
+  const int my = tid / team;
+  const int c = tid - my * team;
+  const bool lane_has_chunk = c < chunks;
+  u32x4 wv = {0u, 0u, 0u, 0u};
+  if (lane_has_chunk) wv = weight[c];
+
+  for (int64_t row0 = (int64_t)blockIdx.x * rows_per_block; row0 < rows;
+       row0 += (int64_t)gridDim.x * rows_per_block) {
+    const int64_t row = row0 + my;
+    const bool act = lane_has_chunk && row < rows;
+    const int64_t off = row * chunks + c;
+    float x[E];
+    float ss = 0.0f;
+    if (act) {
+      u32x4 raw[N + 1];
+      raw[0] = ld_stream(residual + off);
+#pragma unroll
+      for (int i = 0; i < N; ++i) raw[i + 1] = ld_stream(pp.p[i] + off);
+      add_chunk<D, N>(raw, x, ss);
+      st_stream(residual_out + off, narrow(D{}, x));
+    }
+    ss = team_sum(ss, team);
+    const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
+    if (act) st_stream(out + off, scale_chunk<D>(x, inv, wv));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Unfused comparison path, first kernel: reduced = round(sum_i p_i), a flat
+// grid-stride loop over 16-byte chunks (the reduce half of a ReduceScatter
+// written to HBM).
+// ---------------------------------------------------------------------------
+template <class D, int N>
+__global__ void __launch_bounds__(256)
+reduce_kernel(PartialPtrs pp, u32x4* reduced, int64_t total_chunks) {
+  constexpr int E = D::kElems;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
+    u32x4 raw[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) raw[i] = ld_stream(pp.p[i] + c);
+    float acc[E], t[E];
+    widen(D{}, raw[0], acc);
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+      widen(D{}, raw[i], t);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += t[e];
+    }
+    st_stream(reduced + c, narrow(D{}, acc));
+  }
+}
+
+}  // namespace twk

@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI (twnorm_api.hip) and the
+// per-dtype kernel instantiations (twnorm_fused_{bf16,f32}.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "twnorm_kernels.hpp"
+
+namespace twl {
+
+struct FusedArgs {
+  twk::PartialPtrs pp;
+  const twk::u32x4* residual;
+  const twk::u32x4* weight;
+  twk::u32x4* out;
+  twk::u32x4* residual_out;
+  int64_t rows;
+  int chunks;      // 16-byte chunks per row
+  float hidden_f;  // features per row, as float (divisor of the mean square)
+  float eps;
+};
+
+struct Launch {
+  int n;         // partials
+  int waves;     // wide-row kernel: wavefronts per row
+  int k;         // wide-row kernel: chunk slots per lane; 0 = narrow-row kernel
+  int team;      // narrow-row kernel: lanes per row
+  int cu_limit;  // 0: grid covers all rows; > 0: persistent grid for that many CUs
+};
+
+hipError_t launch_fused_bf16(const Launch& L, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused_f32(const Launch& L, const FusedArgs& a, hipStream_t s);
+hipError_t launch_reduce_bf16(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
+                              int64_t total_chunks, int cu_limit, hipStream_t s);
+hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
+                             int64_t total_chunks, int cu_limit, hipStream_t s);
+hipError_t launch_copy(const twk::u32x4* src, twk::u32x4* dst, int64_t chunks, int cu_limit,
+                       hipStream_t s);
+
+}  // namespace twl

@@ -1,0 +1,128 @@
+// Template dispatch from a runtime (n, shape) to a kernel instantiation.
+// Included once per storage format so the two formats compile in parallel.
+#pragma once
+
+#include <algorithm>
+#include <tuple>
+#include <utility>
+
+#include "twnorm_launch.hpp"
+
+namespace twl {
+namespace detail {
+
+// Keep grid * block below 2^31 work-items; the kernels' grid-stride loops
+// cover whatever a smaller grid leaves.
+inline int64_t cap_grid(int64_t grid, int block) {
+  const int64_t max_grid = (int64_t(1) << 31) / block;
+  return std::max<int64_t>(1, std::min(grid, max_grid));
+}
+
+template <typename... P, size_t... I>
+hipError_t launch_tuple(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t s,
+                        std::tuple<P...>& args, std::index_sequence<I...>) {
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(args))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, s);
+}
+
+// Launch `kern` over `work` workgroups, or, with cu_limit > 0, over a
+// persistent grid of cu_limit times the kernel's resident workgroups per CU.
+template <typename... P, typename... A>
+hipError_t go(void (*kern)(P...), int block, int64_t work, int cu_limit, hipStream_t s, A... a) {
+  if (work <= 0) return hipSuccess;
+  int64_t grid = work;
+  if (cu_limit > 0) {
+    int occ = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &occ, reinterpret_cast<const void*>(kern), block, 0);
+    if (e != hipSuccess) return e;
+    grid = std::min<int64_t>(grid, int64_t(cu_limit) * std::max(occ, 1));
+  }
+  grid = cap_grid(grid, block);
+  std::tuple<P...> args(a...);
+  return launch_tuple(kern, dim3(static_cast<uint32_t>(grid)), dim3(block), s, args,
+                      std::index_sequence_for<P...>{});
+}
+
+template <class D, int N>
+hipError_t fused_n(const Launch& L, const FusedArgs& a, hipStream_t s) {
+  const int block = 64 * L.waves;
+#define TW_ROWS(KK)                                                                           \
+  (L.waves <= 4                                                                                \
+       ? go(twk::fused_rows_kernel<D, N, KK, 4>, block, a.rows, L.cu_limit, s, a.pp, a.residual, \
+            a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, a.eps)              \
+       : go(twk::fused_rows_kernel<D, N, KK, 16>, block, a.rows, L.cu_limit, s, a.pp,          \
+            a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, a.eps))
+  switch (L.k) {
+    case 0: {
+      const int rows_per_block = 256 / L.team;
+      return go(twk::fused_team_kernel<D, N>, 256, (a.rows + rows_per_block - 1) / rows_per_block,
+                L.cu_limit, s, a.pp, a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks,
+                L.team, a.hidden_f, a.eps);
+    }
+    case 1: return TW_ROWS(1);
+    case 2: return TW_ROWS(2);
+    case 3: return TW_ROWS(3);
+    case 4: return TW_ROWS(4);
+    case 6: return TW_ROWS(6);
+    case 8: return TW_ROWS(8);
+  }
+#undef TW_ROWS
+  return hipErrorInvalidValue;
+}
+
+template <class D>
+hipError_t fused(const Launch& L, const FusedArgs& a, hipStream_t s) {
+  switch (L.n) {
+    case 1: return fused_n<D, 1>(L, a, s);
+    case 2: return fused_n<D, 2>(L, a, s);
+    case 3: return fused_n<D, 3>(L, a, s);
+    case 4: return fused_n<D, 4>(L, a, s);
+    case 5: return fused_n<D, 5>(L, a, s);
+    case 6: return fused_n<D, 6>(L, a, s);
+    case 7: return fused_n<D, 7>(L, a, s);
+    case 8: return fused_n<D, 8>(L, a, s);
+    case 9: return fused_n<D, 9>(L, a, s);
+    case 10: return fused_n<D, 10>(L, a, s);
+    case 11: return fused_n<D, 11>(L, a, s);
+    case 12: return fused_n<D, 12>(L, a, s);
+    case 13: return fused_n<D, 13>(L, a, s);
+    case 14: return fused_n<D, 14>(L, a, s);
+    case 15: return fused_n<D, 15>(L, a, s);
+    case 16: return fused_n<D, 16>(L, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class D, int N>
+hipError_t reduce_n(const twk::PartialPtrs& pp, twk::u32x4* reduced, int64_t total, int cu_limit,
+                    hipStream_t s) {
+  return go(twk::reduce_kernel<D, N>, 256, (total + 255) / 256, cu_limit, s, pp, reduced, total);
+}
+
+template <class D>
+hipError_t reduce(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced, int64_t total,
+                  int cu_limit, hipStream_t s) {
+  switch (n) {
+    case 1: return reduce_n<D, 1>(pp, reduced, total, cu_limit, s);
+    case 2: return reduce_n<D, 2>(pp, reduced, total, cu_limit, s);
+    case 3: return reduce_n<D, 3>(pp, reduced, total, cu_limit, s);
+    case 4: return reduce_n<D, 4>(pp, reduced, total, cu_limit, s);
+    case 5: return reduce_n<D, 5>(pp, reduced, total, cu_limit, s);
+    case 6: return reduce_n<D, 6>(pp, reduced, total, cu_limit, s);
+    case 7: return reduce_n<D, 7>(pp, reduced, total, cu_limit, s);
+    case 8: return reduce_n<D, 8>(pp, reduced, total, cu_limit, s);
+    case 9: return reduce_n<D, 9>(pp, reduced, total, cu_limit, s);
+    case 10: return reduce_n<D, 10>(pp, reduced, total, cu_limit, s);
+    case 11: return reduce_n<D, 11>(pp, reduced, total, cu_limit, s);
+    case 12: return reduce_n<D, 12>(pp, reduced, total, cu_limit, s);
+    case 13: return reduce_n<D, 13>(pp, reduced, total, cu_limit, s);
+    case 14: return reduce_n<D, 14>(pp, reduced, total, cu_limit, s);
+    case 15: return reduce_n<D, 15>(pp, reduced, total, cu_limit, s);
+    case 16: return reduce_n<D, 16>(pp, reduced, total, cu_limit, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace detail
+}  // namespace twl

@@ -1,0 +1,251 @@
+// Host-side argument validation and launch-shape choice (no HIP calls).
+#include "twnorm_validate.hpp"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace twv {
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+std::atomic<int> g_override_waves{0};
+std::atomic<int> g_override_k{0};
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, int64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Checks shared by every entry point that takes [rows, hidden] tensors.
+tw_status check_shape(int64_t rows, int64_t hidden, tw_dtype dtype, int n_cu_limit,
+                      int64_t* tensor_bytes) {
+  const int b = elem_bytes(dtype);
+  if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+  if (rows < 0) return fail(TW_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
+  if (hidden < 1) return fail(TW_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)hidden);
+  if (n_cu_limit < 0) return fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 0 (got %d)", n_cu_limit);
+  if (hidden > INT64_MAX / 16 / b)
+    return fail(TW_ERR_INVALID_ARG, "hidden %lld too large", (long long)hidden);
+  const int64_t row_bytes = hidden * b;
+  if (rows > 0 && rows > INT64_MAX / row_bytes)
+    return fail(TW_ERR_INVALID_ARG, "rows * hidden overflows 64-bit byte counts");
+  if (row_bytes % 16 != 0)
+    return fail(TW_ERR_UNSUPPORTED, "hidden * sizeof(dtype) = %lld is not a multiple of 16",
+                (long long)row_bytes);
+  if (row_bytes > TW_MAX_HIDDEN_BYTES)
+    return fail(TW_ERR_UNSUPPORTED, "row of %lld bytes exceeds the %d-byte maximum",
+                (long long)row_bytes, TW_MAX_HIDDEN_BYTES);
+  *tensor_bytes = rows * row_bytes;
+  return TW_OK;
+}
+
+tw_status check_partials(const void* const* partials, int n) {
+  if (partials == nullptr) return fail(TW_ERR_INVALID_ARG, "partials array is NULL");
+  if (n < 1 || n > TW_MAX_PARTIALS)
+    return fail(TW_ERR_INVALID_ARG, "n must be in [1, %d] (got %d)", TW_MAX_PARTIALS, n);
+  for (int i = 0; i < n; ++i)
+    if (partials[i] == nullptr) return fail(TW_ERR_INVALID_ARG, "partials[%d] is NULL", i);
+  return TW_OK;
+}
+
+}  // namespace
+
+int elem_bytes(tw_dtype dtype) {
+  switch (dtype) {
+    case TW_BF16: return 2;
+    case TW_F32: return 4;
+  }
+  return 0;
+}
+
+tw_status fail(tw_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+const char* last_error() { return g_err; }
+
+tw_status check_fused(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                      tw_dtype dtype, const void* residual, const void* weight, float eps,
+                      const void* out, const void* residual_out, int n_cu_limit) {
+  tw_status st = check_partials(partials, n);
+  if (st != TW_OK) return st;
+  if (residual == nullptr) return fail(TW_ERR_INVALID_ARG, "residual is NULL");
+  if (weight == nullptr) return fail(TW_ERR_INVALID_ARG, "weight is NULL");
+  if (out == nullptr) return fail(TW_ERR_INVALID_ARG, "out is NULL");
+  if (residual_out == nullptr) return fail(TW_ERR_INVALID_ARG, "residual_out is NULL");
+  if (!(eps >= 0.0f) || std::isinf(eps))
+    return fail(TW_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
+  int64_t tb = 0;
+  st = check_shape(rows, hidden, dtype, n_cu_limit, &tb);
+  if (st != TW_OK) return st;
+  for (int i = 0; i < n; ++i)
+    if (misaligned(partials[i]))
+      return fail(TW_ERR_UNSUPPORTED, "partials[%d] is not 16-byte aligned", i);
+  if (misaligned(residual) || misaligned(weight) || misaligned(out) || misaligned(residual_out))
+    return fail(TW_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+
+  const int64_t wb = hidden * elem_bytes(dtype);
+  const Span s_out = span(out, tb), s_res = span(residual, tb), s_rout = span(residual_out, tb),
+             s_w = span(weight, wb);
+  for (int i = 0; i < n; ++i) {
+    const Span s_p = span(partials[i], tb);
+    if (overlap(s_out, s_p)) return fail(TW_ERR_ALIAS, "out overlaps partials[%d]", i);
+    if (overlap(s_rout, s_p)) return fail(TW_ERR_ALIAS, "residual_out overlaps partials[%d]", i);
+  }
+  if (overlap(s_out, s_res)) return fail(TW_ERR_ALIAS, "out overlaps residual");
+  if (overlap(s_out, s_w)) return fail(TW_ERR_ALIAS, "out overlaps weight");
+  if (overlap(s_out, s_rout)) return fail(TW_ERR_ALIAS, "out overlaps residual_out");
+  if (overlap(s_rout, s_w)) return fail(TW_ERR_ALIAS, "residual_out overlaps weight");
+  if (residual_out != residual && overlap(s_rout, s_res))
+    return fail(TW_ERR_ALIAS, "residual_out partially overlaps residual");
+  return TW_OK;
+}
+
+tw_status check_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                       tw_dtype dtype, const void* reduced, int n_cu_limit) {
+  tw_status st = check_partials(partials, n);
+  if (st != TW_OK) return st;
+  if (reduced == nullptr) return fail(TW_ERR_INVALID_ARG, "reduced is NULL");
+  int64_t tb = 0;
+  st = check_shape(rows, hidden, dtype, n_cu_limit, &tb);
+  if (st != TW_OK) return st;
+  for (int i = 0; i < n; ++i)
+    if (misaligned(partials[i]))
+      return fail(TW_ERR_UNSUPPORTED, "partials[%d] is not 16-byte aligned", i);
+  if (misaligned(reduced)) return fail(TW_ERR_UNSUPPORTED, "reduced is not 16-byte aligned");
+  const Span s_red = span(reduced, tb);
+  for (int i = 0; i < n; ++i)
+    if (partials[i] != reduced && overlap(s_red, span(partials[i], tb)))
+      return fail(TW_ERR_ALIAS, "reduced partially overlaps partials[%d]", i);
+  return TW_OK;
+}
+
+tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_limit) {
+  if (src == nullptr || dst == nullptr) return fail(TW_ERR_INVALID_ARG, "src or dst is NULL");
+  if (bytes < 0) return fail(TW_ERR_INVALID_ARG, "bytes must be >= 0");
+  if (n_cu_limit < 0) return fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 0");
+  if (bytes % 16 != 0) return fail(TW_ERR_UNSUPPORTED, "bytes must be a multiple of 16");
+  if (misaligned(src) || misaligned(dst))
+    return fail(TW_ERR_UNSUPPORTED, "src and dst must be 16-byte aligned");
+  if (overlap(span(src, bytes), span(dst, bytes))) return fail(TW_ERR_ALIAS, "src and dst overlap");
+  return TW_OK;
+}
+
+// Automatic shape: rows of at most 32 chunks go to the narrow-row kernel with
+// the smallest power-of-two team that covers them.  Wider rows take the
+// (waves, k) with the fewest idle chunk slots, ties broken by kPreferK.
+static const int kAllowedK[] = {1, 2, 3, 4, 6, 8};
+static const int kPreferK[] = {2, 4, 1, 3, 8, 6};
+
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, Shape* shape) {
+  const int b = elem_bytes(dtype);
+  if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
+  const int64_t chunks = hidden * b / 16;
+  const int ow = g_override_waves.load(), ok = g_override_k.load();
+  if (ow > 0 && ok > 0) {
+    if ((int64_t)ow * 64 * ok < chunks)
+      return fail(TW_ERR_UNSUPPORTED, "forced shape %d waves x %d chunks cannot cover %lld chunks",
+                  ow, ok, (long long)chunks);
+    *shape = Shape{ow, ok, 0};
+    return TW_OK;
+  }
+  if (chunks <= 32) {
+    int team = 1;
+    while (team < chunks) team <<= 1;
+    *shape = Shape{0, 0, team};
+    return TW_OK;
+  }
+  int best_w = 0, best_k = 0;
+  int64_t best_waste = -1;
+  for (int k : kPreferK) {
+    const int64_t w = (chunks + 64 * k - 1) / (64 * k);
+    if (w > 16) continue;
+    const int64_t waste = w * 64 * k - chunks;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      best_w = (int)w;
+      best_k = k;
+    }
+  }
+  if (best_waste < 0)
+    return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide", (long long)hidden);
+  *shape = Shape{best_w, best_k, 0};
+  return TW_OK;
+}
+
+tw_status set_override(int waves, int k) {
+  bool k_ok = (k == 0);
+  for (int a : kAllowedK) k_ok = k_ok || (a == k);
+  if (waves < 0 || waves > 16 || !k_ok || ((waves == 0) != (k == 0)))
+    return fail(TW_ERR_INVALID_ARG, "invalid forced shape (%d waves, %d chunks per lane)", waves, k);
+  g_override_waves.store(waves);
+  g_override_k.store(k);
+  return TW_OK;
+}
+
+}  // namespace twv
+
+// ---------------------------------------------------------------------------
+// HIP-free exported entry points
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* tw_status_string(tw_status s) {
+  switch (s) {
+    case TW_OK: return "TW_OK";
+    case TW_ERR_INVALID_ARG: return "TW_ERR_INVALID_ARG";
+    case TW_ERR_UNSUPPORTED: return "TW_ERR_UNSUPPORTED";
+    case TW_ERR_ALIAS: return "TW_ERR_ALIAS";
+    case TW_ERR_HIP: return "TW_ERR_HIP";
+  }
+  return "TW_UNKNOWN_STATUS";
+}
+
+const char* tw_last_error(void) { return twv::last_error(); }
+
+int tw_abi_version(void) { return TW_ABI_VERSION; }
+
+tw_status tw_set_fused_shape(int waves, int chunks_per_lane) {
+  twv::clear_error();
+  return twv::set_override(waves, chunks_per_lane);
+}
+
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int* waves, int* chunks_per_lane,
+                               int* team_lanes) {
+  twv::clear_error();
+  if (waves == nullptr || chunks_per_lane == nullptr || team_lanes == nullptr)
+    return twv::fail(TW_ERR_INVALID_ARG, "output pointer is NULL");
+  const int b = twv::elem_bytes(dtype);
+  if (b == 0) return twv::fail(TW_ERR_INVALID_ARG, "unknown dtype");
+  if (hidden < 1) return twv::fail(TW_ERR_INVALID_ARG, "hidden must be >= 1");
+  if ((hidden * b) % 16 != 0) return twv::fail(TW_ERR_UNSUPPORTED, "row bytes not a multiple of 16");
+  if (hidden * b > TW_MAX_HIDDEN_BYTES) return twv::fail(TW_ERR_UNSUPPORTED, "row too wide");
+  twv::Shape s{};
+  tw_status st = twv::choose_shape(dtype, hidden, &s);
+  if (st != TW_OK) return st;
+  *waves = s.waves;
+  *chunks_per_lane = s.k;
+  *team_lanes = s.team;
+  return TW_OK;
+}
+
+}  // extern "C"

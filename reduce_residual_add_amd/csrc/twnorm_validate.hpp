@@ -1,0 +1,41 @@
+// Host-side argument validation and launch-shape choice for libtwnorm.
+// HIP-free: this translation unit makes no HIP call and includes no HIP
+// header, so every error path of the C ABI can be exercised without a GPU.
+#pragma once
+
+#include <stdint.h>
+
+#include "twnorm.h"
+
+namespace twv {
+
+// Kernel launch shape for one token row.
+//   k > 0 : wide-row kernel, `waves` wavefronts per row, k chunk slots/lane
+//   k == 0: narrow-row kernel, `team` lanes per row (power of two <= 32)
+struct Shape {
+  int waves;
+  int k;
+  int team;
+};
+
+int elem_bytes(tw_dtype dtype);  // 0 for an unknown dtype
+
+// Record a failure message for tw_last_error() and return `s`.
+tw_status fail(tw_status s, const char* fmt, ...);
+void clear_error();
+const char* last_error();
+
+tw_status check_fused(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                      tw_dtype dtype, const void* residual, const void* weight, float eps,
+                      const void* out, const void* residual_out, int n_cu_limit);
+tw_status check_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                       tw_dtype dtype, const void* reduced, int n_cu_limit);
+tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_limit);
+
+// Shape for (dtype, hidden); honours the tw_set_fused_shape override.
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, Shape* shape);
+
+// Force (waves, k) for wide rows; (0, 0) restores the automatic choice.
+tw_status set_override(int waves, int k);
+
+}  // namespace twv

@@ -1,0 +1,81 @@
+"""Shared helpers of the GPU parity tests: moving seeded storage arrays to
+the device and back, and the tolerance of the comparison.
+
+Tolerance (the reading of "max abs error <= 2e-2 and max rel error <= 1e-2
+for bf16, <= 1e-5 relative for fp32"):
+  bf16: element passes iff |got - ref| <= max(2e-2, 1e-2 * |ref|)
+  fp32: element passes iff |got - ref| <= 1e-5 * max(1, |ref|)
+The literal conjunction cannot hold for any correct kernel: a relative bound
+is meaningless at |ref| ~ 0, and one bf16 half-ulp above 8 is 0.031 > 2e-2.
+Every bf16 result is also checked to lie within one bf16 ulp of the oracle's
+correctly rounded value (float32 accumulation error is far below half an
+ulp, so only rounding-boundary cases may differ by one).
+"""
+import numpy as np
+
+from oracle import twnorm_oracle as O
+
+
+def to_dev(arr, dtype, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def from_dev(t, dtype):
+    import torch
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().astype(np.float32)
+
+
+def inputs_to_dev(inp, device="cuda"):
+    dt = inp["dtype"]
+    parts = [to_dev(p, dt, device) for p in inp["partials"]]
+    return parts, to_dev(inp["residual"], dt, device), to_dev(inp["weight"], dt, device)
+
+
+def tolerance_report(got_storage, ref, dtype):
+    """Returns dict(fails, max_abs, max_rel, max_ulp) for stored results vs
+    float64 oracle values."""
+    got = O.decode(got_storage, dtype)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = np.abs(got - ref)
+    if dtype == "bf16":
+        bound = np.maximum(2e-2, 1e-2 * np.abs(ref))
+    else:
+        bound = 1e-5 * np.maximum(1.0, np.abs(ref))
+    big = np.abs(ref) >= 1.0
+    rep = dict(fails=int(np.count_nonzero(~(d <= bound))),
+               max_abs=float(d.max()) if d.size else 0.0,
+               max_rel=float((d[big] / np.abs(ref[big])).max()) if np.any(big) else 0.0)
+    if dtype == "bf16":
+        rep["max_ulp"] = int(bf16_ulp_distance(got_storage, O.bf16_encode_rne(ref)).max()) if d.size else 0
+    return rep
+
+
+def bf16_ulp_distance(a_bits, b_bits):
+    """Distance in representable bf16 steps between two bit arrays."""
+    def ordered(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + u)
+    return np.abs(ordered(np.asarray(a_bits)) - ordered(np.asarray(b_bits)))
+
+
+def assert_parity(got_storage, ref, dtype, what=""):
+    rep = tolerance_report(got_storage, ref, dtype)
+    assert rep["fails"] == 0, f"{what}: {rep}"
+    if dtype == "bf16":
+        assert rep["max_ulp"] <= 1, f"{what}: more than one bf16 ulp from the oracle: {rep}"
+    return rep
+
+
+def sample_rows(rows, k=384, seed=0):
+    """First, last and a seeded sample of rows (all rows if few)."""
+    if rows <= k:
+        return np.arange(rows)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(rows, size=k - 4, replace=False).tolist()) | {0, 1, rows - 2, rows - 1}
+    return np.array(sorted(pick))

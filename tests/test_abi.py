@@ -1,0 +1,183 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/twnorm.h declares, and every error path returns its status before
+any HIP call.  Pointers here are fake, 16-byte aligned addresses that the
+validator compares but never dereferences."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twnorm.h")
+
+import reduce_residual_add_amd as twn  # noqa: E402
+
+OK, INV, UNS, ALIAS = twn.TW_OK, twn.TW_ERR_INVALID_ARG, twn.TW_ERR_UNSUPPORTED, twn.TW_ERR_ALIAS
+BF16, F32 = twn.TW_BF16, twn.TW_F32
+
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tw_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(twn.LIB_PATH):
+        pytest.fail("libtwnorm.so is not built (run __graft_entry__.build())")
+    return twn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert "tw_fused_reduce_rmsnorm" in declared and "tw_reduce" in declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in twnorm.h but not exported"
+    assert sorted(twn.EXPORTED) == declared
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tw_abi_version() == twn.TW_ABI_VERSION
+    for code, name in [(OK, b"TW_OK"), (INV, b"TW_ERR_INVALID_ARG"), (UNS, b"TW_ERR_UNSUPPORTED"),
+                       (ALIAS, b"TW_ERR_ALIAS"), (twn.TW_ERR_HIP, b"TW_ERR_HIP")]:
+        assert lib.tw_status_string(code) == name
+
+
+class Bufs:
+    """Fake, disjoint, 16-byte aligned device addresses."""
+
+    def __init__(self, n=2, rows=4, hidden=64, dtype=BF16):
+        self.n, self.rows, self.hidden, self.dtype = n, rows, hidden, dtype
+        base = 0x7F0000000000
+        self.parts = [base + i * 64 * MB for i in range(n)]
+        self.residual = base + 1024 * MB
+        self.weight = base + 1100 * MB
+        self.out = base + 1200 * MB
+        self.res_out = base + 1300 * MB
+
+    def fused(self, lib, **kw):
+        a = dict(parts=self.parts, n=self.n, rows=self.rows, hidden=self.hidden, dtype=self.dtype,
+                 residual=self.residual, weight=self.weight, eps=1e-5, out=self.out,
+                 res_out=self.res_out, cu=0)
+        a.update(kw)
+        parts = a["parts"]
+        arr = None if parts is None else (ctypes.c_void_p * max(1, len(parts)))(*parts)
+        return lib.tw_fused_reduce_rmsnorm(arr, a["n"], a["rows"], a["hidden"], a["dtype"],
+                                           a["residual"], a["weight"], a["eps"], a["out"],
+                                           a["res_out"], a["cu"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(parts=None), INV),
+    (dict(n=0), INV),
+    (dict(n=17), INV),
+    (dict(rows=-1), INV),
+    (dict(hidden=0), INV),
+    (dict(hidden=-64), INV),
+    (dict(eps=-1e-5), INV),
+    (dict(eps=float("nan")), INV),
+    (dict(eps=float("inf")), INV),
+    (dict(cu=-1), INV),
+    (dict(dtype=7), INV),
+    (dict(residual=None), INV),
+    (dict(weight=None), INV),
+    (dict(out=None), INV),
+    (dict(res_out=None), INV),
+    (dict(hidden=12), UNS),                 # 24 bytes per row: not a multiple of 16
+    (dict(hidden=16 * 64 * 8 * 8 + 8), UNS),  # row beyond the widest shape
+    (dict(hidden=1 << 60), INV),            # byte count overflow
+], ids=lambda v: str(v))
+def test_fused_invalid_args(lib, kw, expect):
+    st = Bufs().fused(lib, **kw)
+    assert st == expect, (kw, st, twn.last_error())
+    assert twn.last_error() != ""
+
+
+def test_fused_null_partial_and_misaligned(lib):
+    b = Bufs()
+    assert b.fused(lib, parts=[b.parts[0], None]) == INV
+    assert b.fused(lib, parts=[b.parts[0] + 8, b.parts[1]]) == UNS
+    assert b.fused(lib, residual=b.residual + 2) == UNS
+    assert b.fused(lib, weight=b.weight + 4) == UNS
+    assert b.fused(lib, out=b.out + 8) == UNS
+    assert b.fused(lib, res_out=b.res_out + 8) == UNS
+    assert b.fused(lib, dtype=F32, hidden=6) == UNS     # 24 bytes
+
+
+def test_fused_alias_rules(lib):
+    b = Bufs()
+    tensor = b.rows * b.hidden * 2
+    assert b.fused(lib, out=b.parts[1]) == ALIAS
+    assert b.fused(lib, out=b.residual) == ALIAS
+    assert b.fused(lib, out=b.weight) == ALIAS
+    assert b.fused(lib, out=b.res_out) == ALIAS
+    assert b.fused(lib, out=b.residual + tensor - 16) == ALIAS       # partial overlap
+    assert b.fused(lib, res_out=b.parts[0]) == ALIAS
+    assert b.fused(lib, res_out=b.weight) == ALIAS
+    assert b.fused(lib, res_out=b.residual + 16) == ALIAS            # shifted in-place
+    # exact in-place residual update is allowed; rows == 0 is a no-op, so
+    # these return OK without a HIP call
+    assert b.fused(lib, res_out=b.residual, rows=0) == OK
+    assert b.fused(lib, rows=0) == OK
+    # partials may repeat (reading a buffer twice is harmless)
+    assert b.fused(lib, parts=[b.parts[0], b.parts[0]], rows=0) == OK
+    # adjacent (touching, not overlapping) buffers are fine
+    assert b.fused(lib, out=b.residual + tensor, rows=0) == OK
+
+
+def test_reduce_rmsnorm_copy_validation(lib):
+    b = Bufs()
+    arr = (ctypes.c_void_p * 2)(*b.parts)
+    assert lib.tw_reduce(arr, 0, 4, 64, BF16, b.out, 0, None) == INV
+    assert lib.tw_reduce(arr, 2, 4, 64, BF16, None, 0, None) == INV
+    assert lib.tw_reduce(arr, 2, 4, 64, BF16, b.parts[1] + 16, 0, None) == ALIAS
+    assert lib.tw_reduce(arr, 2, 0, 64, BF16, b.parts[1], 0, None) == OK  # in place, no-op
+    assert lib.tw_reduce(arr, 2, 4, 60, BF16, b.out, 0, None) == UNS
+    assert lib.tw_rmsnorm(None, 4, 64, BF16, b.residual, b.weight, 1e-5, b.out, b.res_out, 0,
+                          None) == INV
+    assert lib.tw_rmsnorm(b.parts[0], 4, 64, BF16, b.residual, b.weight, 1e-5, b.parts[0],
+                          b.res_out, 0, None) == ALIAS
+    assert lib.tw_rmsnorm(b.parts[0], 0, 64, BF16, b.residual, b.weight, 1e-5, b.out,
+                          b.residual, 0, None) == OK
+    assert lib.tw_stream_copy(b.parts[0], b.parts[1], 100, 0, None) == UNS
+    assert lib.tw_stream_copy(b.parts[0], b.parts[0] + 16, 1024, 0, None) == ALIAS
+    assert lib.tw_stream_copy(None, b.parts[1], 1024, 0, None) == INV
+    assert lib.tw_stream_copy(b.parts[0], b.parts[1], 0, 0, None) == OK
+
+
+def test_error_is_cleared_by_next_call(lib):
+    b = Bufs()
+    assert b.fused(lib, n=0) == INV
+    assert twn.last_error() != ""
+    assert b.fused(lib, rows=0) == OK
+    assert twn.last_error() == ""
+
+
+def test_shape_choice(lib):
+    # (dtype, hidden) -> (waves, chunks per lane, team lanes)
+    assert twn.query_fused_shape(F32, 64) == (0, 0, 16)      # 16 chunks: narrow-row team
+    assert twn.query_fused_shape(BF16, 8) == (0, 0, 1)
+    assert twn.query_fused_shape(BF16, 256) == (0, 0, 32)
+    w, k, t = twn.query_fused_shape(BF16, 8192)
+    assert t == 0 and w * 64 * k >= 1024 and w <= 16
+    w, k, t = twn.query_fused_shape(BF16, 5120)
+    assert t == 0 and w * 64 * k >= 640
+    w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8)   # the widest row
+    assert (w, k) == (16, 8)
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(BF16, 12)
+    # forced shapes
+    twn.set_fused_shape(8, 2)
+    try:
+        assert twn.query_fused_shape(BF16, 8192) == (8, 2, 0)
+        with pytest.raises(twn.TwError):
+            twn.query_fused_shape(BF16, 16384)   # 8 x 64 x 2 < 2048 chunks
+    finally:
+        twn.set_fused_shape(0, 0)
+    for bad in [(17, 1), (4, 5), (0, 2), (2, 0), (-1, 1)]:
+        with pytest.raises(twn.TwError):
+            twn.set_fused_shape(*bad)

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
+the same seeded inputs.  Needs an MI355X; every case prints what it runs
+before touching the GPU."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import twnorm_oracle as O
+from gpu_helpers import (assert_parity, bf16_ulp_distance, from_dev, inputs_to_dev, sample_rows,
+                         to_dev, tolerance_report)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _oracle_rows(inp, rows_idx):
+    dt = inp["dtype"]
+    parts = [O.decode(p[rows_idx], dt) for p in inp["partials"]]
+    return O.fused(parts, O.decode(inp["residual"][rows_idx], dt), O.decode(inp["weight"], dt),
+                   O.eps_as_passed(inp["eps"]))
+
+
+def _run_fused(twn, inp, n_cu_limit=0, in_place=False):
+    import torch
+    parts, res, w = inputs_to_dev(inp)
+    out = torch.full_like(res, 7.0)
+    res_out = res if in_place else torch.full_like(res, 7.0)
+    twn.fused_reduce_rmsnorm(parts, res, w, inp["eps"], out=out, residual_out=res_out,
+                             n_cu_limit=n_cu_limit)
+    torch.cuda.synchronize()
+    return from_dev(out, inp["dtype"]), from_dev(res_out, inp["dtype"])
+
+
+# ---------------------------------------------------------------------------
+# Every workload at its full size (oracle on a row sample; rows are
+# independent), in the launch configurations the benchmark times.
+# ---------------------------------------------------------------------------
+CASES = [(w.name, cu) for w in workloads.WORKLOADS for cu in w.cu_limits]
+
+
+@pytest.mark.parametrize("name,cu", CASES, ids=[f"{n}-cu{c}" for n, c in CASES])
+def test_fused_full_size(twn, name, cu):
+    w = workloads.get(name)
+    _say(f"[fused full] {name} n={w.n} rows={w.rows} H={w.hidden} {w.dtype} n_cu_limit={cu}")
+    inp = workloads.make(w, seed=0)
+    out, res_out = _run_fused(twn, inp, n_cu_limit=cu)
+    idx = sample_rows(w.rows)
+    ref_out, ref_res = _oracle_rows(inp, idx)
+    assert_parity(res_out[idx], ref_res, w.dtype, f"{name} residual_out")
+    assert_parity(out[idx], ref_out, w.dtype, f"{name} out")
+
+
+# ---------------------------------------------------------------------------
+# Smaller shapes the oracle checks in full: several tiles, ragged tails,
+# every kernel shape (narrow-row teams, 1..16 waves, 1..8 chunks per lane).
+# ---------------------------------------------------------------------------
+SHAPES = [
+    # (n, rows, hidden, dtype)
+    (1, 5, 8, "bf16"),        # one chunk per row: team of 1 lane
+    (2, 37, 64, "f32"),       # 16 chunks: team of 16
+    (3, 33, 200, "bf16"),     # 25 chunks: team of 32, 7 idle lanes
+    (2, 9, 256, "bf16"),      # 32 chunks
+    (5, 17, 520, "bf16"),     # 65 chunks: first wide-row shape, ragged
+    (4, 64, 1000, "f32"),     # 250 chunks
+    (2, 129, 4096, "bf16"),
+    (4, 50, 5120, "bf16"),    # 640 chunks
+    (8, 40, 8192, "bf16"),
+    (7, 23, 8200, "bf16"),    # 1025 chunks: one slot past a round shape
+    (16, 11, 3072, "bf16"),   # the most partials
+    (3, 13, 12288, "f32"),    # 3072 chunks, fp32
+    (2, 3, 65536, "bf16"),    # the widest supported row
+    (9, 1, 1024, "bf16"),     # a single row
+]
+
+
+@pytest.mark.parametrize("n,rows,hidden,dtype", SHAPES, ids=[f"n{a}-r{b}-h{c}-{d}" for a, b, c, d in SHAPES])
+def test_fused_shapes(twn, n, rows, hidden, dtype):
+    _say(f"[fused shape] n={n} rows={rows} H={hidden} {dtype} shape={twn.query_fused_shape(0 if dtype == 'bf16' else 1, hidden)}")
+    inp = workloads.make_random(n, rows, hidden, dtype, seed=hidden + n)
+    out, res_out = _run_fused(twn, inp)
+    ref_out, ref_res = O.fused_from_storage(inp)
+    assert_parity(res_out, ref_res, dtype, "residual_out")
+    assert_parity(out, ref_out, dtype, "out")
+
+
+@pytest.mark.parametrize("waves,k", [(16, 1), (8, 2), (4, 4), (6, 3), (3, 6), (2, 8), (1, 8), (5, 4)])
+def test_fused_forced_shapes(twn, waves, k):
+    """Every wide-row instantiation (both launch bounds) gives oracle parity."""
+    import torch
+    _say(f"[forced shape] waves={waves} k={k}")
+    inp = workloads.make_random(8, 19, 4096, "bf16", seed=waves * 10 + k)
+    twn.set_fused_shape(waves, k)
+    try:
+        out, res_out = _run_fused(twn, inp)
+    finally:
+        twn.set_fused_shape(0, 0)
+    ref_out, ref_res = O.fused_from_storage(inp)
+    assert_parity(res_out, ref_res, "bf16", "residual_out")
+    assert_parity(out, ref_out, "bf16", "out")
+    del torch
+
+
+# ---------------------------------------------------------------------------
+# Unfused comparison path
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "page1", "zero_padded", "shard70b"])
+def test_unfused_pair(twn, name):
+    import torch
+    w = workloads.get(name)
+    rows = min(w.rows, 512)
+    _say(f"[unfused] {name} rows={rows}")
+    inp = workloads.make(w, seed=2, rows=rows)
+    parts, res, wt = inputs_to_dev(inp)
+    red = twn.reduce(parts)
+    out, res_out = twn.rmsnorm(red, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    red_h = from_dev(red, w.dtype)
+    # reduce alone: the stored sum of the partials
+    assert_parity(red_h, O.reduce_from_storage(inp), w.dtype, "reduce")
+    # the pair end to end against the fused definition (the intermediate's
+    # rounding is inside the tolerance)
+    ref_out, ref_res = O.fused_from_storage(inp)
+    rep = tolerance_report(from_dev(out, w.dtype), ref_out, w.dtype)
+    assert rep["fails"] == 0, rep
+    rep = tolerance_report(from_dev(res_out, w.dtype), ref_res, w.dtype)
+    assert rep["fails"] == 0, rep
+
+
+def test_rmsnorm_alone(twn):
+    """tw_rmsnorm on a seeded `reduced` tensor (not one the GPU produced)."""
+    import torch
+    _say("[rmsnorm alone]")
+    inp = workloads.make_random(1, 77, 5120, "bf16", seed=99)
+    red, res, wt = inputs_to_dev(inp)
+    out, res_out = twn.rmsnorm(red[0], res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    ref_out, ref_res = O.rmsnorm_from_storage(inp["partials"][0], inp)
+    assert_parity(from_dev(res_out, "bf16"), ref_res, "bf16", "residual_out")
+    assert_parity(from_dev(out, "bf16"), ref_out, "bf16", "out")
+
+
+# ---------------------------------------------------------------------------
+# Zero-padded column partials: exact arithmetic makes these bit-exact
+# ---------------------------------------------------------------------------
+def test_zero_padded_bit_exact(twn):
+    import torch
+    w = workloads.get("zero_padded")
+    _say("[zero-padded bit-exact] full size")
+    inp = workloads.make(w, seed=0)
+    parts, res, wt = inputs_to_dev(inp)
+    red = twn.reduce(parts)
+    out, res_out = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    block = w.hidden // w.n
+    concat = np.concatenate([inp["partials"][i][:, i * block:(i + 1) * block] for i in range(w.n)], axis=1)
+    # each column has one nonzero partial, so the sum is that partial exactly
+    assert np.array_equal(from_dev(red, "bf16"), concat)
+    # residual_out = RNE(p_k + r): float32 holds p_k + r exactly when the
+    # exponents are within 15 of each other; check those elements bit-exactly
+    pk = O.decode(concat, "bf16")
+    r = O.decode(inp["residual"], "bf16")
+    exact_sum = pk + r
+    f32_exact = exact_sum.astype(np.float32).astype(np.float64) == exact_sum
+    got = from_dev(res_out, "bf16")
+    expect = O.bf16_encode_rne(exact_sum)
+    assert f32_exact.mean() > 0.99
+    assert np.array_equal(got[f32_exact], expect[f32_exact])
+
+
+# ---------------------------------------------------------------------------
+# Determinism: the same row gives the same bits under any sharding, CU limit,
+# repetition or in-place choice.
+# ---------------------------------------------------------------------------
+def test_determinism(twn):
+    import torch
+    w = workloads.get("shard70b")
+    _say("[determinism] shard70b")
+    inp = workloads.make(w, seed=5, rows=512)
+    parts, res, wt = inputs_to_dev(inp)
+    base_out, base_res = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    b_out, b_res = from_dev(base_out, "bf16"), from_dev(base_res, "bf16")
+    # repeated calls
+    for _ in range(3):
+        o, r = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(o, "bf16"), b_out) and np.array_equal(from_dev(r, "bf16"), b_res)
+    # CU limits
+    for cu in (8, 16, 32, 1, 255, 0):
+        _say(f"[determinism] n_cu_limit={cu}")
+        o, r = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], n_cu_limit=cu)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(o, "bf16"), b_out), cu
+        assert np.array_equal(from_dev(r, "bf16"), b_res), cu
+    # token shards: row ranges through pointer offsets (views), stitched back
+    cuts = [0, 1, 130, 131, 400, 512]
+    out = torch.empty_like(res)
+    res_out = torch.empty_like(res)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        twn.fused_reduce_rmsnorm([p[a:b] for p in parts], res[a:b], wt, inp["eps"],
+                                 out=out[a:b], residual_out=res_out[a:b])
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out, "bf16"), b_out)
+    assert np.array_equal(from_dev(res_out, "bf16"), b_res)
+    # in place residual update
+    res2 = res.clone()
+    o, r = twn.fused_reduce_rmsnorm(parts, res2, wt, inp["eps"], residual_out=res2)
+    torch.cuda.synchronize()
+    assert r.data_ptr() == res2.data_ptr()
+    assert np.array_equal(from_dev(o, "bf16"), b_out)
+    assert np.array_equal(from_dev(res2, "bf16"), b_res)
+
+
+def test_rmsnorm_equals_fused_with_one_partial(twn):
+    import torch
+    _say("[rmsnorm == fused n=1]")
+    inp = workloads.make_random(1, 64, 8192, "bf16", seed=3)
+    parts, res, wt = inputs_to_dev(inp)
+    o1, r1 = twn.rmsnorm(parts[0], res, wt, 1e-5)
+    o2, r2 = twn.fused_reduce_rmsnorm(parts, res, wt, 1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(r1, r2)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+def test_zero_rows_is_noop(twn):
+    import torch
+    _say("[edge] rows=0")
+    p = torch.zeros((0, 4096), dtype=torch.bfloat16, device="cuda")
+    res = torch.zeros_like(p)
+    w = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    out, res_out = twn.fused_reduce_rmsnorm([p, p], res, w, 1e-5)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4096)
+
+
+def test_special_values(twn):
+    """eps = 0 on an all-zero row gives NaN (0 * inf), as in the oracle; a NaN
+    or inf in one row stays in that row; the paired worked-example rows come
+    out as the hand-derived values."""
+    import torch
+    _say("[edge] special values")
+    h = 64
+    rows = 4
+    p0 = np.zeros((rows, h), np.float32)
+    p1 = np.zeros((rows, h), np.float32)
+    r = np.zeros((rows, h), np.float32)
+    # row 0: all zero -> NaN with eps = 0
+    # row 1: hand-derived case, mean square 4 -> [1, -1, 1, 1] * w over 4 columns x 16
+    r[1] = np.tile([1, 1, -1, 1], 16)
+    p0[1] = np.tile([1, -3, 0, 0], 16)
+    p1[1] = np.tile([0, 0, 3, 1], 16)
+    # row 2: contains inf
+    p0[2] = 1.0
+    p0[2, 5] = np.inf
+    # row 3: ordinary values
+    p0[3] = np.linspace(-2, 2, h)
+    for dt in ("f32", "bf16"):
+        store = (lambda a: a) if dt == "f32" else (lambda a: O.bf16_encode_rne(a.astype(np.float64)))
+        w = np.ones(h, np.float32)
+        parts = [to_dev(store(p0), dt), to_dev(store(p1), dt)]
+        out, res_out = twn.fused_reduce_rmsnorm(parts, to_dev(store(r), dt), to_dev(store(w), dt), 0.0)
+        torch.cuda.synchronize()
+        o = O.decode(from_dev(out, dt), dt)
+        assert np.all(np.isnan(o[0]))
+        assert np.array_equal(o[1], np.tile([1.0, -1.0, 1.0, 1.0], 16))
+        assert np.all(np.isnan(o[2]) | (o[2] == 0))   # inf / inf -> NaN, finite / inf -> 0
+        ref = O.rmsnorm(O.decode(store(p0[3:4]), dt), np.ones(h), 0.0)
+        assert tolerance_report(from_dev(out, dt)[3:4], ref, dt)["fails"] == 0
