@@ -31,6 +31,7 @@ METRIC = "fused reduce+RMSNorm HBM GB/s (% of peak) and token-rows/s at H=8192, 
 PEAK_GBS = 8000.0              # MI355X HBM3E, published
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+COPY_CAL_BYTES = 512 * 1024 * 1024   # plain copy of known size for counter scaling
 KERNEL_SOURCES = ["reduce_residual_add_amd/csrc/twnorm_kernels.hpp",
                   "reduce_residual_add_amd/csrc/twnorm_launch_impl.hpp",
                   "reduce_residual_add_amd/csrc/twnorm_validate.cpp"]
@@ -71,6 +72,9 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--report", default="", help="write a detailed JSON report here")
+    p.add_argument("--calibration-copies", type=int, default=0,
+                   help="after the timed steps, run this many plain copies of "
+                        f"{COPY_CAL_BYTES >> 20} MiB (hardware-counter calibration)")
     return p.parse_args(argv)
 
 
@@ -117,21 +121,23 @@ def n_rotating_sets(set_bytes, requested):
     return s
 
 
-def time_steps(step_fns, steps, warmup):
-    """Warm up, then time exactly `steps` calls between two events on the
-    current stream; returns (ms per step, wall seconds)."""
+def time_steps(step_fns, steps, warmup, stream=None):
+    """Warm up, then time exactly `steps` calls between two events recorded
+    on the stream the kernels run on (default: the current stream), with a
+    device synchronisation on both sides; returns (ms per step, wall s)."""
     import torch
     n = len(step_fns)
     for i in range(warmup):
         step_fns[i % n]()
     torch.cuda.synchronize()
+    s = stream if stream is not None else torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    start.record()
+    start.record(s)
     for i in range(steps):
         step_fns[i % n]()
-    end.record()
+    end.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
@@ -219,10 +225,13 @@ def _from_dev(t, dtype):
 # ---------------------------------------------------------------------------
 
 
-def measure_fused(twn, w, sets, cu, steps, warmup):
-    fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"], n_cu_limit=cu)
-           for d in sets]
-    ms, wall = time_steps(fns, steps, warmup)
+def measure_fused(twn, w, sets, cu, steps, warmup, stream=None):
+    """Per-step time of the fused call.  With cu > 0 and `stream` the
+    library's CU-masked stream, the kernels are queued and timed there
+    directly (no per-call join to another stream)."""
+    fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"],
+                             n_cu_limit=cu, stream=stream) for d in sets]
+    ms, wall = time_steps(fns, steps, warmup, stream=stream)
     return ms, wall
 
 
@@ -265,7 +274,8 @@ def main(argv=None):
     n_sets = n_rotating_sets(set_bytes, args.rotate)
     sets = make_sets(inp, n_sets)
 
-    ms, wall = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup)
+    masked = twn.cu_masked_stream(args.cu) if args.cu > 0 else None
+    ms, wall = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup, stream=masked)
     bytes_call = w.fused_bytes()
     gbs = bytes_call / (ms * 1e-3) / 1e9
     rows_per_s = w.rows / (ms * 1e-3)
@@ -293,6 +303,21 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": counter_traffic(w.name)},
     }
+    if args.cu > 0:
+        # the same calls issued from the default stream: each one pays the
+        # event join to the masked stream and back
+        jms, _ = measure_fused(twn, w, sets, args.cu, max(20, args.steps // 5), 5)
+        result["ms_per_step_joined_from_default_stream"] = round(jms, 6)
+
+    if args.calibration_copies > 0:
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(args.calibration_copies):
+            twn.stream_copy(src, dst)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = COPY_CAL_BYTES
+        del src, dst
 
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()

@@ -38,8 +38,9 @@
  *                                    n_cu_limit < 0, unknown dtype, or
  *                                    rows * hidden too large for 64-bit bytes.
  *                TW_ERR_UNSUPPORTED  hidden * sizeof(dtype) not a multiple of
- *                                    16, a pointer not 16-byte aligned, or
- *                                    hidden beyond TW_MAX_HIDDEN_BYTES bytes.
+ *                                    16, a pointer not 16-byte aligned,
+ *                                    hidden beyond TW_MAX_HIDDEN_BYTES bytes,
+ *                                    or a fourth distinct n_cu_limit.
  *                TW_ERR_ALIAS        an output overlaps an input it may not
  *                                    (rules per entry point below).
  *                TW_ERR_HIP          a HIP runtime call or the launch failed;
@@ -51,6 +52,9 @@
  *              k in [1, CUs) runs the kernel on at most k CUs (persistent grid
  *              on a cached CU-masked stream, ordered after and before `stream`
  *              by events).  Results are bit-identical for every n_cu_limit.
+ *              Each distinct k needs a hardware queue of its own for the life
+ *              of the process: at most 3 distinct k per device and process;
+ *              a fourth returns TW_ERR_UNSUPPORTED.
  *   Determinism The summation order depends only on (dtype, hidden, n): the
  *              same row gives the same bits whatever rows, shard offset or
  *              n_cu_limit are.
@@ -133,6 +137,19 @@ tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_lim
                          void* stream);
 
 /*
+ * The library's CU-masked stream for `n_cu_limit` on the current device
+ * (created on first use, owned by the library for the life of the process;
+ * never destroy it).  Its kernels run only on the CUs of the first
+ * n_cu_limit mask bits, which the hardware spreads round-robin over the 8
+ * XCDs and then their shader engines.  Calls made on this stream with the
+ * same n_cu_limit launch directly, without the per-call event join to the
+ * caller's stream: a caller can queue a batch of calls there and order the
+ * batch against its other streams itself.  n_cu_limit must be in [1, CUs).
+ * Counts toward the 3 distinct limits a process may use.
+ */
+tw_status tw_cu_masked_stream(int n_cu_limit, void** stream);
+
+/*
  * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts
  * per token row with `chunks_per_lane` 16-byte chunks per lane (both 0 =
  * automatic choice).  Applies to every later call on every thread; a shape
@@ -143,10 +160,10 @@ tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_lim
  */
 tw_status tw_set_fused_shape(int waves, int chunks_per_lane);
 
-/* Launch shape the fused kernel would use for (dtype, hidden); writes the
- * wavefronts per row and chunks per lane (team_lanes for rows narrower than
- * one wavefront, else 0).  HIP-free. */
-tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int* waves,
+/* Launch shape the fused kernel would use for (dtype, hidden, n partials);
+ * writes the wavefronts per row and chunks per lane (team_lanes for rows
+ * narrower than one wavefront, else 0).  HIP-free. */
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves,
                                int* chunks_per_lane, int* team_lanes);
 
 const char* tw_status_string(tw_status s);

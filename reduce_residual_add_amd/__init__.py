@@ -43,6 +43,7 @@ _STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
                  TW_ERR_HIP: "TW_ERR_HIP"}
 
 EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_reduce", "tw_rmsnorm", "tw_stream_copy",
+            "tw_cu_masked_stream",
             "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
             "tw_last_error", "tw_abi_version")
 
@@ -66,9 +67,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_rmsnorm.restype = _c.c_int
     lib.tw_stream_copy.argtypes = [_vp, _vp, _i64, _c.c_int, _vp]
     lib.tw_stream_copy.restype = _c.c_int
+    lib.tw_cu_masked_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
+    lib.tw_cu_masked_stream.restype = _c.c_int
     lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int]
     lib.tw_set_fused_shape.restype = _c.c_int
-    lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.POINTER(_c.c_int),
+    lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.c_int, _c.POINTER(_c.c_int),
                                          _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]
     lib.tw_query_fused_shape.restype = _c.c_int
     lib.tw_status_string.argtypes = [_c.c_int]
@@ -233,16 +236,27 @@ def stream_copy(src, dst, *, n_cu_limit: int = 0, stream=None):
     return dst
 
 
+def cu_masked_stream(n_cu_limit: int):
+    """The library's CU-masked stream for `n_cu_limit` CUs, as a torch
+    ExternalStream.  Calls issued on it with the same n_cu_limit skip the
+    per-call event join (order it against other streams yourself)."""
+    torch = _torch()
+    h = _vp()
+    _check(load().tw_cu_masked_stream(int(n_cu_limit), ctypes.byref(h)))
+    return torch.cuda.ExternalStream(h.value)
+
+
 def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0) -> None:
     """Force the fused kernel's launch shape (0, 0 = automatic)."""
     _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane)))
 
 
-def query_fused_shape(dtype: int, hidden: int):
-    """(waves, chunks_per_lane, team_lanes) the fused kernel uses."""
+def query_fused_shape(dtype: int, hidden: int, n: int):
+    """(waves, chunks_per_lane, team_lanes) the fused kernel uses for n
+    partials of rows `hidden` wide."""
     w, k, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    _check(load().tw_query_fused_shape(int(dtype), int(hidden), ctypes.byref(w), ctypes.byref(k),
-                                       ctypes.byref(t)))
+    _check(load().tw_query_fused_shape(int(dtype), int(hidden), int(n), ctypes.byref(w),
+                                       ctypes.byref(k), ctypes.byref(t)))
     return w.value, k.value, t.value
 
 

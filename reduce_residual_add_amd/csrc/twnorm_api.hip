@@ -8,6 +8,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -28,7 +29,11 @@ struct DeviceState {
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
 
+// Report a failed HIP call.  HIP also keeps the error as the thread's sticky
+// "last error"; it is read back and cleared here so that it cannot surface
+// later in an unrelated caller's launch check.
 tw_status hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();
   return twv::fail(TW_ERR_HIP, "%s: %s (hipError %d)", what, hipGetErrorString(e),
                    static_cast<int>(e));
 }
@@ -56,14 +61,47 @@ tw_status device_state(DeviceState** out) {
   return TW_OK;
 }
 
+// CU count of the current device, cached per device without a lock.
+tw_status current_device_cus(int* cus_out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus_out = c;
+      return TW_OK;
+    }
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+  if (cus < 1) return twv::fail(TW_ERR_HIP, "device reports %d CUs", cus);
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  *cus_out = cus;
+  return TW_OK;
+}
+
 // A stream whose kernels may only occupy the CUs of the first `k` mask bits.
-// Streams keep the default priority.  Caller holds g_mu.
+// Streams keep the default priority.  Each CU-masked stream owns a hardware
+// queue of its own, and a process gets few of them (4 by default, shared
+// with the ordinary streams), so at most kMaxMaskedStreams distinct limits
+// are cached per device, for the life of the process; creating and
+// destroying queues on every call is avoided on purpose.  Caller holds g_mu.
+constexpr size_t kMaxMaskedStreams = 3;
+
 tw_status masked_stream(DeviceState& d, int k, hipStream_t* out) {
   auto it = d.masked.find(k);
   if (it != d.masked.end()) {
     *out = it->second;
     return TW_OK;
   }
+  if (d.masked.size() >= kMaxMaskedStreams)
+    return twv::fail(TW_ERR_UNSUPPORTED,
+                     "n_cu_limit %d: this process already uses %zu distinct CU limits (the "
+                     "maximum; each needs its own hardware queue)",
+                     k, d.masked.size());
   std::vector<uint32_t> mask((d.cus + 31) / 32, 0u);
   for (int i = 0; i < k; ++i) mask[i / 32] |= 1u << (i % 32);
   hipStream_t s = nullptr;
@@ -92,6 +130,11 @@ tw_status run(int n_cu_limit, hipStream_t caller, const char* what, F&& launch) 
   hipStream_t ms = nullptr;
   st = masked_stream(*d, n_cu_limit, &ms);
   if (st != TW_OK) return st;
+  if (caller == ms) {
+    // already on the masked stream (tw_cu_masked_stream): no join needed
+    const hipError_t le = launch(n_cu_limit, ms);
+    return le == hipSuccess ? TW_OK : hip_fail(le, what);
+  }
   hipError_t e = hipEventRecord(d->ev_in, caller);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = hipStreamWaitEvent(ms, d->ev_in, 0);
@@ -112,7 +155,10 @@ tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t h
   if (st != TW_OK) return st;
   if (rows == 0) return TW_OK;
   twv::Shape sh{};
-  st = twv::choose_shape(dtype, hidden, &sh);
+  st = twv::choose_shape(dtype, hidden, n, &sh);
+  if (st != TW_OK) return st;
+  int cus = 0;
+  st = current_device_cus(&cus);
   if (st != TW_OK) return st;
 
   twl::FusedArgs a{};
@@ -125,12 +171,11 @@ tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t h
   a.chunks = static_cast<int>(hidden * twv::elem_bytes(dtype) / 16);
   a.hidden_f = static_cast<float>(hidden);
   a.eps = eps;
-  twl::Launch L{n, sh.waves, sh.k, sh.team, 0};
+  twl::Launch L{n, sh.waves, sh.k, sh.team, 0, cus};
   return run(n_cu_limit, static_cast<hipStream_t>(stream), "fused kernel launch",
              [&](int cu, hipStream_t s) {
                L.cu_limit = cu;
-               return dtype == TW_BF16 ? twl::launch_fused_bf16(L, a, s)
-                                       : twl::launch_fused_f32(L, a, s);
+               return twl::launch_fused(dtype == TW_BF16, L, a, s);
              });
 }
 
@@ -171,6 +216,24 @@ tw_status tw_reduce(const void* const* partials, int n, int64_t rows, int64_t hi
                return dtype == TW_BF16 ? twl::launch_reduce_bf16(n, pp, red, total, cu, s)
                                        : twl::launch_reduce_f32(n, pp, red, total, cu, s);
              });
+}
+
+tw_status tw_cu_masked_stream(int n_cu_limit, void** stream) {
+  twv::clear_error();
+  if (stream == nullptr) return twv::fail(TW_ERR_INVALID_ARG, "stream is NULL");
+  if (n_cu_limit < 1) return twv::fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 1");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceState* d = nullptr;
+  tw_status st = device_state(&d);
+  if (st != TW_OK) return st;
+  if (n_cu_limit >= d->cus)
+    return twv::fail(TW_ERR_INVALID_ARG, "n_cu_limit %d is not below the device's %d CUs",
+                     n_cu_limit, d->cus);
+  hipStream_t ms = nullptr;
+  st = masked_stream(*d, n_cu_limit, &ms);
+  if (st != TW_OK) return st;
+  *stream = static_cast<void*>(ms);
+  return TW_OK;
 }
 
 tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit, void* stream) {

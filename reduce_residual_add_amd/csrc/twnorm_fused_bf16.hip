@@ -1,10 +1,11 @@
-// Kernel instantiations for bf16 storage (float32 arithmetic).
+// bf16 storage (float32 arithmetic): fused kernels for 1..8 partials and
+// the unfused reduce kernel.
 #include "twnorm_launch_impl.hpp"
 
 namespace twl {
 
-hipError_t launch_fused_bf16(const Launch& L, const FusedArgs& a, hipStream_t s) {
-  return detail::fused<twk::Bf16>(L, a, s);
+hipError_t launch_fused_bf16_n1to8(const Launch& L, const FusedArgs& a, hipStream_t s) {
+  return detail::fused_range<twk::Bf16, 1, 8>(L, a, s);
 }
 
 hipError_t launch_reduce_bf16(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,

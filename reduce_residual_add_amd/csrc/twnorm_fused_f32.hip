@@ -1,4 +1,5 @@
-// Kernel instantiations for float32 storage, plus the streaming copy.
+// float32 storage: fused kernels for 1..8 partials and the unfused reduce
+// kernel; plus the streaming copy.
 #include "twnorm_launch_impl.hpp"
 
 namespace twk {
@@ -28,8 +29,8 @@ stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64
 
 namespace twl {
 
-hipError_t launch_fused_f32(const Launch& L, const FusedArgs& a, hipStream_t s) {
-  return detail::fused<twk::F32>(L, a, s);
+hipError_t launch_fused_f32_n1to8(const Launch& L, const FusedArgs& a, hipStream_t s) {
+  return detail::fused_range<twk::F32, 1, 8>(L, a, s);
 }
 
 hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,

@@ -22,15 +22,24 @@ struct FusedArgs {
 };
 
 struct Launch {
-  int n;         // partials
-  int waves;     // wide-row kernel: wavefronts per row
-  int k;         // wide-row kernel: chunk slots per lane; 0 = narrow-row kernel
-  int team;      // narrow-row kernel: lanes per row
-  int cu_limit;  // 0: grid covers all rows; > 0: persistent grid for that many CUs
+  int n;           // partials
+  int waves;       // wide-row kernel: wavefronts per row
+  int k;           // wide-row kernel: chunk slots per lane; 0 = narrow-row kernel
+  int team;        // narrow-row kernel: lanes per row
+  int cu_limit;    // 0: whole chip; > 0: persistent grid for that many CUs
+  int device_cus;  // CUs of the device (persistent grid of the wide-row kernel)
 };
 
-hipError_t launch_fused_bf16(const Launch& L, const FusedArgs& a, hipStream_t s);
-hipError_t launch_fused_f32(const Launch& L, const FusedArgs& a, hipStream_t s);
+// n in [1, 8] and [9, 16] are instantiated in separate translation units.
+hipError_t launch_fused_bf16_n1to8(const Launch& L, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused_bf16_n9to16(const Launch& L, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused_f32_n1to8(const Launch& L, const FusedArgs& a, hipStream_t s);
+hipError_t launch_fused_f32_n9to16(const Launch& L, const FusedArgs& a, hipStream_t s);
+
+inline hipError_t launch_fused(bool bf16, const Launch& L, const FusedArgs& a, hipStream_t s) {
+  if (bf16) return L.n <= 8 ? launch_fused_bf16_n1to8(L, a, s) : launch_fused_bf16_n9to16(L, a, s);
+  return L.n <= 8 ? launch_fused_f32_n1to8(L, a, s) : launch_fused_f32_n9to16(L, a, s);
+}
 hipError_t launch_reduce_bf16(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
                               int64_t total_chunks, int cu_limit, hipStream_t s);
 hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -25,18 +27,39 @@ hipError_t launch_tuple(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t s
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, 0, s);
 }
 
-// Launch `kern` over `work` workgroups, or, with cu_limit > 0, over a
-// persistent grid of cu_limit times the kernel's resident workgroups per CU.
+// Resident workgroups per CU of (kernel, block size), looked up once.
+inline hipError_t resident_per_cu(const void* kern, int block, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({kern, block});
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, block, 0);
+  if (e != hipSuccess) return e;
+  occ = std::max(occ, 1);
+  cache[{kern, block}] = occ;
+  *out = occ;
+  return hipSuccess;
+}
+
+// Launch `kern` over `work` workgroups.  With persistent_cus > 0 the grid is
+// capped at the workgroups that many CUs hold at once (the kernels loop over
+// the rest): the CU-limited mode, and the fused kernel's persistent,
+// software-pipelined row loop.
 template <typename... P, typename... A>
-hipError_t go(void (*kern)(P...), int block, int64_t work, int cu_limit, hipStream_t s, A... a) {
+hipError_t go(void (*kern)(P...), int block, int64_t work, int persistent_cus, hipStream_t s,
+              A... a) {
   if (work <= 0) return hipSuccess;
   int64_t grid = work;
-  if (cu_limit > 0) {
+  if (persistent_cus > 0) {
     int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ, reinterpret_cast<const void*>(kern), block, 0);
+    hipError_t e = resident_per_cu(reinterpret_cast<const void*>(kern), block, &occ);
     if (e != hipSuccess) return e;
-    grid = std::min<int64_t>(grid, int64_t(cu_limit) * std::max(occ, 1));
+    grid = std::min<int64_t>(grid, int64_t(persistent_cus) * occ);
   }
   grid = cap_grid(grid, block);
   std::tuple<P...> args(a...);
@@ -47,12 +70,19 @@ hipError_t go(void (*kern)(P...), int block, int64_t work, int cu_limit, hipStre
 template <class D, int N>
 hipError_t fused_n(const Launch& L, const FusedArgs& a, hipStream_t s) {
   const int block = 64 * L.waves;
-#define TW_ROWS(KK)                                                                           \
-  (L.waves <= 4                                                                                \
-       ? go(twk::fused_rows_kernel<D, N, KK, 4>, block, a.rows, L.cu_limit, s, a.pp, a.residual, \
-            a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, a.eps)              \
-       : go(twk::fused_rows_kernel<D, N, KK, 16>, block, a.rows, L.cu_limit, s, a.pp,          \
-            a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, a.eps))
+  const int64_t work_rows = a.rows;
+  // wide rows: persistent grid on the CU limit, else on the whole chip
+  const int grid_cus = L.cu_limit > 0 ? L.cu_limit : L.device_cus;
+#define TW_ROWS(KK)                                                                            \
+  (L.waves <= 4   ? go(twk::fused_rows_kernel<D, N, KK, 4>, block, work_rows, grid_cus, s, a.pp,  \
+                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.eps)                                                                   \
+   : L.waves <= 8 ? go(twk::fused_rows_kernel<D, N, KK, 8>, block, work_rows, grid_cus, s, a.pp,  \
+                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.eps)                                                                   \
+                  : go(twk::fused_rows_kernel<D, N, KK, 16>, block, work_rows, grid_cus, s, a.pp, \
+                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.eps))
   switch (L.k) {
     case 0: {
       const int rows_per_block = 256 / L.team;
@@ -71,26 +101,19 @@ hipError_t fused_n(const Launch& L, const FusedArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <class D>
-hipError_t fused(const Launch& L, const FusedArgs& a, hipStream_t s) {
+// Dispatch on the partial count; NLO..NHI bounds the instantiations made by
+// one translation unit (the ranges compile in parallel).
+template <class D, int NLO, int NHI>
+hipError_t fused_range(const Launch& L, const FusedArgs& a, hipStream_t s) {
+#define TW_N(NN) \
+  case NN:       \
+    if constexpr (NN >= NLO && NN <= NHI) return fused_n<D, NN>(L, a, s); \
+    break;
   switch (L.n) {
-    case 1: return fused_n<D, 1>(L, a, s);
-    case 2: return fused_n<D, 2>(L, a, s);
-    case 3: return fused_n<D, 3>(L, a, s);
-    case 4: return fused_n<D, 4>(L, a, s);
-    case 5: return fused_n<D, 5>(L, a, s);
-    case 6: return fused_n<D, 6>(L, a, s);
-    case 7: return fused_n<D, 7>(L, a, s);
-    case 8: return fused_n<D, 8>(L, a, s);
-    case 9: return fused_n<D, 9>(L, a, s);
-    case 10: return fused_n<D, 10>(L, a, s);
-    case 11: return fused_n<D, 11>(L, a, s);
-    case 12: return fused_n<D, 12>(L, a, s);
-    case 13: return fused_n<D, 13>(L, a, s);
-    case 14: return fused_n<D, 14>(L, a, s);
-    case 15: return fused_n<D, 15>(L, a, s);
-    case 16: return fused_n<D, 16>(L, a, s);
+    TW_N(1) TW_N(2) TW_N(3) TW_N(4) TW_N(5) TW_N(6) TW_N(7) TW_N(8)
+    TW_N(9) TW_N(10) TW_N(11) TW_N(12) TW_N(13) TW_N(14) TW_N(15) TW_N(16)
   }
+#undef TW_N
   return hipErrorInvalidValue;
 }
 

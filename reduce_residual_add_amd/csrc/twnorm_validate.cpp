@@ -150,15 +150,42 @@ tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_l
   return TW_OK;
 }
 
-// Automatic shape: rows of at most 32 chunks go to the narrow-row kernel with
-// the smallest power-of-two team that covers them.  Wider rows take the
-// (waves, k) with the fewest idle chunk slots, ties broken by kPreferK.
-static const int kAllowedK[] = {1, 2, 3, 4, 6, 8};
-static const int kPreferK[] = {2, 4, 1, 3, 8, 6};
+// Register-fit table of the wide-row kernels, generated at build time from the
+// compiler's resource remarks (see build.py): which chunk counts K run without
+// scratch for each (dtype, n, launch bound).
+#include "twnorm_fit_table.inc"
 
-tw_status choose_shape(tw_dtype dtype, int64_t hidden, Shape* shape) {
+static const int kAllowedK[] = {1, 2, 3, 4, 6, 8};
+// Among spill-free shapes with the fewest idle chunk slots, this order of K
+// breaks ties (measured on MI355X: fewer, wider wavefronts per row lose
+// latency hiding; more chunk slots per lane cost registers).
+static const int kPreferK[] = {2, 1, 4, 3, 6, 8};
+
+static int k_index(int k) {
+  for (int i = 0; i < 6; ++i)
+    if (kKValues[i] == k) return i;
+  return -1;
+}
+
+static int bucket_of(int waves) { return waves <= 4 ? 0 : (waves <= 8 ? 1 : 2); }
+
+bool shape_spills(tw_dtype dtype, int n, int waves, int k) {
+  const int ki = k_index(k);
+  if (ki < 0 || n < 1 || n > 16) return true;
+  const int dt = dtype == TW_BF16 ? 0 : 1;
+  return ((kFitMask[dt][n][bucket_of(waves)] >> ki) & 1) == 0;
+}
+
+// Automatic shape: rows of at most 32 chunks go to the narrow-row kernel with
+// the smallest power-of-two team that covers them.  Wider rows take, for each
+// K, the fewest wavefronts W <= 16 that cover the row; among the (W, K) whose
+// kernel spills nothing, the fewest idle chunk slots win, ties broken by
+// kPreferK.  If every candidate spills (very wide rows with many partials),
+// the fewest idle slots win regardless.
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
   const int b = elem_bytes(dtype);
   if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
+  if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
   const int64_t chunks = hidden * b / 16;
   const int ow = g_override_waves.load(), ok = g_override_k.load();
   if (ow > 0 && ok > 0) {
@@ -174,21 +201,25 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, Shape* shape) {
     *shape = Shape{0, 0, team};
     return TW_OK;
   }
-  int best_w = 0, best_k = 0;
-  int64_t best_waste = -1;
+  int best_w = 0, best_k = 0, any_w = 0, any_k = 0;
+  int64_t best_waste = -1, any_waste = -1;
   for (int k : kPreferK) {
     const int64_t w = (chunks + 64 * k - 1) / (64 * k);
     if (w > 16) continue;
     const int64_t waste = w * 64 * k - chunks;
-    if (best_waste < 0 || waste < best_waste) {
+    if (any_waste < 0 || waste < any_waste) {
+      any_waste = waste;
+      any_w = (int)w;
+      any_k = k;
+    }
+    if (!shape_spills(dtype, n, (int)w, k) && (best_waste < 0 || waste < best_waste)) {
       best_waste = waste;
       best_w = (int)w;
       best_k = k;
     }
   }
-  if (best_waste < 0)
-    return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide", (long long)hidden);
-  *shape = Shape{best_w, best_k, 0};
+  if (any_waste < 0) return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide", (long long)hidden);
+  *shape = best_waste >= 0 ? Shape{best_w, best_k, 0} : Shape{any_w, any_k, 0};
   return TW_OK;
 }
 
@@ -229,8 +260,8 @@ tw_status tw_set_fused_shape(int waves, int chunks_per_lane) {
   return twv::set_override(waves, chunks_per_lane);
 }
 
-tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int* waves, int* chunks_per_lane,
-                               int* team_lanes) {
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves,
+                               int* chunks_per_lane, int* team_lanes) {
   twv::clear_error();
   if (waves == nullptr || chunks_per_lane == nullptr || team_lanes == nullptr)
     return twv::fail(TW_ERR_INVALID_ARG, "output pointer is NULL");
@@ -240,7 +271,7 @@ tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int* waves, int* 
   if ((hidden * b) % 16 != 0) return twv::fail(TW_ERR_UNSUPPORTED, "row bytes not a multiple of 16");
   if (hidden * b > TW_MAX_HIDDEN_BYTES) return twv::fail(TW_ERR_UNSUPPORTED, "row too wide");
   twv::Shape s{};
-  tw_status st = twv::choose_shape(dtype, hidden, &s);
+  tw_status st = twv::choose_shape(dtype, hidden, n, &s);
   if (st != TW_OK) return st;
   *waves = s.waves;
   *chunks_per_lane = s.k;

@@ -32,8 +32,12 @@ tw_status check_reduce(const void* const* partials, int n, int64_t rows, int64_t
                        tw_dtype dtype, const void* reduced, int n_cu_limit);
 tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_limit);
 
-// Shape for (dtype, hidden); honours the tw_set_fused_shape override.
-tw_status choose_shape(tw_dtype dtype, int64_t hidden, Shape* shape);
+// Shape for (dtype, hidden, n); honours the tw_set_fused_shape override.
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape);
+
+// True if the wide-row kernel for (dtype, n, waves, k) needs scratch memory
+// (from the build's register-fit table).
+bool shape_spills(tw_dtype dtype, int n, int waves, int k);
 
 // Force (waves, k) for wide rows; (0, 0) restores the automatic choice.
 tw_status set_override(int waves, int k);

@@ -149,6 +149,13 @@ def test_reduce_rmsnorm_copy_validation(lib):
     assert lib.tw_stream_copy(b.parts[0], b.parts[1], 0, 0, None) == OK
 
 
+def test_masked_stream_argument_checks(lib):
+    h = ctypes.c_void_p()
+    assert lib.tw_cu_masked_stream(8, None) == INV
+    assert lib.tw_cu_masked_stream(0, ctypes.byref(h)) == INV
+    assert lib.tw_cu_masked_stream(-3, ctypes.byref(h)) == INV
+
+
 def test_error_is_cleared_by_next_call(lib):
     b = Bufs()
     assert b.fused(lib, n=0) == INV
@@ -158,26 +165,67 @@ def test_error_is_cleared_by_next_call(lib):
 
 
 def test_shape_choice(lib):
-    # (dtype, hidden) -> (waves, chunks per lane, team lanes)
-    assert twn.query_fused_shape(F32, 64) == (0, 0, 16)      # 16 chunks: narrow-row team
-    assert twn.query_fused_shape(BF16, 8) == (0, 0, 1)
-    assert twn.query_fused_shape(BF16, 256) == (0, 0, 32)
-    w, k, t = twn.query_fused_shape(BF16, 8192)
-    assert t == 0 and w * 64 * k >= 1024 and w <= 16
-    w, k, t = twn.query_fused_shape(BF16, 5120)
+    # (dtype, hidden, n) -> (waves, chunks per lane, team lanes)
+    assert twn.query_fused_shape(F32, 64, 2) == (0, 0, 16)      # 16 chunks: narrow-row team
+    assert twn.query_fused_shape(BF16, 8, 1) == (0, 0, 1)
+    assert twn.query_fused_shape(BF16, 256, 3) == (0, 0, 32)
+    w, k, t = twn.query_fused_shape(BF16, 8192, 8)
+    assert t == 0 and w * 64 * k == 1024 and w <= 16
+    w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
-    w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8)   # the widest row
+    w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8, 2)   # the widest row
     assert (w, k) == (16, 8)
     with pytest.raises(twn.TwError):
-        twn.query_fused_shape(BF16, 12)
+        twn.query_fused_shape(BF16, 12, 2)
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(BF16, 1024, 17)
     # forced shapes
     twn.set_fused_shape(8, 2)
     try:
-        assert twn.query_fused_shape(BF16, 8192) == (8, 2, 0)
+        assert twn.query_fused_shape(BF16, 8192, 8) == (8, 2, 0)
         with pytest.raises(twn.TwError):
-            twn.query_fused_shape(BF16, 16384)   # 8 x 64 x 2 < 2048 chunks
+            twn.query_fused_shape(BF16, 16384, 8)   # 8 x 64 x 2 < 2048 chunks
     finally:
         twn.set_fused_shape(0, 0)
     for bad in [(17, 1), (4, 5), (0, 2), (2, 0), (-1, 1)]:
         with pytest.raises(twn.TwError):
             twn.set_fused_shape(*bad)
+
+
+K_VALUES = [1, 2, 3, 4, 6, 8]
+
+
+def _fit_table():
+    """kFitMask[dtype][n][bucket] from the include the build generated out
+    of the compiler's kernel-resource-usage remarks."""
+    import numpy as np
+    path = os.path.join(ROOT, "_build", "twnorm_fit_table.inc")
+    if not os.path.exists(path):
+        pytest.skip("build products not present")
+    text = open(path).read()
+    m = re.search(r"kFitMask\[2\]\[17\]\[3\] = \{(.*?)\n\};", text, re.S)
+    return np.array([int(x) for x in re.findall(r"\d+", m.group(1))]).reshape(2, 17, 3)
+
+
+def _bucket(w):
+    return 0 if w <= 4 else (1 if w <= 8 else 2)
+
+
+def test_auto_shapes_never_spill(lib):
+    """Whenever some (waves, K) covering the row runs without scratch, the
+    automatic choice is one of those."""
+    mask = _fit_table()
+    for dt, b in ((BF16, 2), (F32, 4)):
+        for n in range(1, 17):
+            for chunks in list(range(33, 200, 7)) + [256, 512, 640, 1000, 1024, 1025, 2048, 3072,
+                                                      4096, 6000, 8192]:
+                hidden = chunks * 16 // b
+                w, k, t = twn.query_fused_shape(dt, hidden, n)
+                assert t == 0 and w * 64 * k >= chunks and w <= 16
+                free = [(-(-chunks // (64 * kk)), kk) for kk in K_VALUES
+                        if -(-chunks // (64 * kk)) <= 16 and
+                        (mask[dt][n][_bucket(-(-chunks // (64 * kk)))] >> K_VALUES.index(kk)) & 1]
+                if free:
+                    assert (mask[dt][n][_bucket(w)] >> K_VALUES.index(k)) & 1, (dt, n, hidden, w, k)
+                    # and it wastes no more chunk slots than any spill-free option
+                    assert w * 64 * k - chunks == min(ww * 64 * kk - chunks for ww, kk in free)
