@@ -152,13 +152,15 @@ tw_status tw_cu_masked_stream(int n_cu_limit, void** stream);
 /*
  * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts
  * per token row with `chunks_per_lane` 16-byte chunks per lane (both 0 =
- * automatic choice).  Applies to every later call on every thread; a shape
- * that cannot cover a row returns TW_ERR_UNSUPPORTED at the call.  Changing
- * the shape may change the last bit of results (a different reduction tree).
- * Returns TW_ERR_INVALID_ARG for waves outside [0,16] or chunks_per_lane not
- * in {0,1,2,3,4,6,8}.
+ * automatic choice), and cap the persistent grid at `wgs_per_cu` workgroups
+ * per CU (0 = as many as the CU holds).  Applies to every later call on every
+ * thread; a shape that cannot cover a row returns TW_ERR_UNSUPPORTED at the
+ * call.  Changing the shape may change the last bit of results (a different
+ * reduction tree); the grid cap never does.  Returns TW_ERR_INVALID_ARG for
+ * waves outside [0,16], chunks_per_lane not in {0,1,2,3,4,6,8}, only one of
+ * the two being 0, or wgs_per_cu < 0.
  */
-tw_status tw_set_fused_shape(int waves, int chunks_per_lane);
+tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu);
 
 /* Launch shape the fused kernel would use for (dtype, hidden, n partials);
  * writes the wavefronts per row and chunks per lane (team_lanes for rows

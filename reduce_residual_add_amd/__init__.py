@@ -69,7 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_stream_copy.restype = _c.c_int
     lib.tw_cu_masked_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
     lib.tw_cu_masked_stream.restype = _c.c_int
-    lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int]
+    lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int, _c.c_int]
     lib.tw_set_fused_shape.restype = _c.c_int
     lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.c_int, _c.POINTER(_c.c_int),
                                          _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]
@@ -246,9 +246,10 @@ def cu_masked_stream(n_cu_limit: int):
     return torch.cuda.ExternalStream(h.value)
 
 
-def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0) -> None:
-    """Force the fused kernel's launch shape (0, 0 = automatic)."""
-    _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane)))
+def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0, wgs_per_cu: int = 0) -> None:
+    """Force the fused kernel's launch shape (0, 0 = automatic) and cap its
+    persistent grid at wgs_per_cu workgroups per CU (0 = no cap)."""
+    _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane), int(wgs_per_cu)))
 
 
 def query_fused_shape(dtype: int, hidden: int, n: int):

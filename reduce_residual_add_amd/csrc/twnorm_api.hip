@@ -171,7 +171,7 @@ tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t h
   a.chunks = static_cast<int>(hidden * twv::elem_bytes(dtype) / 16);
   a.hidden_f = static_cast<float>(hidden);
   a.eps = eps;
-  twl::Launch L{n, sh.waves, sh.k, sh.team, 0, cus};
+  twl::Launch L{n, sh.waves, sh.k, sh.team, 0, cus, twv::wgs_per_cu_cap()};
   return run(n_cu_limit, static_cast<hipStream_t>(stream), "fused kernel launch",
              [&](int cu, hipStream_t s) {
                L.cu_limit = cu;

@@ -74,6 +74,29 @@ __device__ __forceinline__ void st_stream(u32x4* p, u32x4 v) {
 #endif
 }
 
+// Buffer-resource access (the wide-row kernel).  A descriptor in four scalar
+// registers holds a row's base address and byte size; lanes pass a 32-bit
+// byte offset.  Per row only the scalar base changes, so no lane does 64-bit
+// address arithmetic, and the buffer unit's range check turns lanes past the
+// row's end into zero loads and dropped stores.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer access
+constexpr int kCpolNt = 2;              // cache-policy bit "nt" (non-temporal)
+constexpr int kLoadCpol = TW_NT_LOADS ? kCpolNt : 0;
+constexpr int kStoreCpol = TW_NT_STORES ? kCpolNt : 0;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load(rsrc_t r, unsigned byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kLoadCpol);
+}
+
+__device__ __forceinline__ void buf_store(u32x4 v, rsrc_t r, unsigned byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kStoreCpol);
+}
+
 // ---------------------------------------------------------------------------
 // Format conversion.  bf16 -> f32 is exact (the bf16 bits are the high half
 // of a float32).  f32 -> bf16 uses v_cvt_pk_bf16_f32: round to nearest even,
@@ -193,22 +216,16 @@ __device__ __forceinline__ u32x4 scale_chunk(const float* x, float inv, const u3
 // ---------------------------------------------------------------------------
 template <int N, int K>
 __device__ __forceinline__ void load_row(u32x4 (&raw)[K][N + 1], const PartialPtrs& pp,
-                                         const u32x4* residual, int64_t base, int tid, int nthr,
-                                         int chunks) {
-  // Row base pointers are wavefront-uniform (scalar registers); lanes add a
-  // 32-bit chunk offset, so loads use the saddr + voffset form.
-  const u32x4* r_row = residual + base;
-  const u32x4* p_row[N];
+                                         const u32x4* residual, int64_t base, int row_bytes,
+                                         unsigned lane_off, unsigned slot_stride) {
+  const rsrc_t r_row = make_rsrc(residual + base, row_bytes);
 #pragma unroll
-  for (int i = 0; i < N; ++i) p_row[i] = pp.p[i] + base;
+  for (int k = 0; k < K; ++k) raw[k][0] = buf_load(r_row, lane_off + k * slot_stride);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const unsigned c = unsigned(tid + k * nthr);
-    if (c < unsigned(chunks)) {
-      raw[k][0] = ld_stream(r_row + c);
+  for (int i = 0; i < N; ++i) {
+    const rsrc_t p_row = make_rsrc(pp.p[i] + base, row_bytes);
 #pragma unroll
-      for (int i = 0; i < N; ++i) raw[k][i + 1] = ld_stream(p_row[i] + c);
-    }
+    for (int k = 0; k < K; ++k) raw[k][i + 1] = buf_load(p_row, lane_off + k * slot_stride);
   }
 }
 
@@ -223,35 +240,36 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
   const int nthr = blockDim.x;
   const int wave = tid >> 6;
   const int nwaves = nthr >> 6;
+  const int row_bytes = chunks * 16;
+  const unsigned lane_off = unsigned(tid) * 16u;      // this lane's first chunk
+  const unsigned slot_stride = unsigned(nthr) * 16u;  // between a lane's chunk slots
 
   u32x4 wv[K];
+  const rsrc_t w_rsrc = make_rsrc(weight, row_bytes);
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int c = tid + k * nthr;
-    if (c < chunks) wv[k] = weight[c];
-  }
+  for (int k = 0; k < K; ++k) wv[k] = buf_load(w_rsrc, lane_off + k * slot_stride);
 
   u32x4 raw[K][N + 1];
   int64_t row = blockIdx.x;
-  if (row < rows) load_row<N, K>(raw, pp, residual, row * chunks, tid, nthr, chunks);
+  if (row < rows) load_row<N, K>(raw, pp, residual, row * chunks, row_bytes, lane_off, slot_stride);
   int parity = 0;
   for (; row < rows; row += gridDim.x) {
     const int64_t base = row * chunks;
-    u32x4* ro_row = residual_out + base;
-    u32x4* o_row = out + base;
+    const rsrc_t ro_rsrc = make_rsrc(residual_out + base, row_bytes);
+    const rsrc_t o_rsrc = make_rsrc(out + base, row_bytes);
+    // Slots past the row's end loaded zeros, so they add nothing to ss, and
+    // their stores fall outside the descriptor's range and are dropped.
     float x[K][E];
     float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const unsigned c = unsigned(tid + k * nthr);
-      if (c < unsigned(chunks)) {
-        add_chunk<D, N>(raw[k], x[k], ss);
-        st_stream(ro_row + c, narrow(D{}, x[k]));
-      }
+      add_chunk<D, N>(raw[k], x[k], ss);
+      buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
     }
     // The raw registers are free again: start the next row's loads now.
     const int64_t next = row + gridDim.x;
-    if (next < rows) load_row<N, K>(raw, pp, residual, next * chunks, tid, nthr, chunks);
+    if (next < rows)
+      load_row<N, K>(raw, pp, residual, next * chunks, row_bytes, lane_off, slot_stride);
 
     ss = team_sum(ss, 64);
     if (MAXW > 1 && nwaves > 1) {
@@ -266,10 +284,8 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
     }
     const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const unsigned c = unsigned(tid + k * nthr);
-      if (c < unsigned(chunks)) st_stream(o_row + c, scale_chunk<D>(x[k], inv, wv[k]));
-    }
+    for (int k = 0; k < K; ++k)
+      buf_store(scale_chunk<D>(x[k], inv, wv[k]), o_rsrc, lane_off + k * slot_stride);
   }
 }
 

@@ -28,6 +28,7 @@ struct Launch {
   int team;        // narrow-row kernel: lanes per row
   int cu_limit;    // 0: whole chip; > 0: persistent grid for that many CUs
   int device_cus;  // CUs of the device (persistent grid of the wide-row kernel)
+  int wgs_per_cu;  // cap on resident workgroups per CU of that grid (0 = none)
 };
 
 // n in [1, 8] and [9, 16] are instantiated in separate translation units.

@@ -51,20 +51,27 @@ inline hipError_t resident_per_cu(const void* kern, int block, int* out) {
 // the rest): the CU-limited mode, and the fused kernel's persistent,
 // software-pipelined row loop.
 template <typename... P, typename... A>
-hipError_t go(void (*kern)(P...), int block, int64_t work, int persistent_cus, hipStream_t s,
-              A... a) {
+hipError_t go_capped(void (*kern)(P...), int block, int64_t work, int persistent_cus,
+                     int per_cu_cap, hipStream_t s, A... a) {
   if (work <= 0) return hipSuccess;
   int64_t grid = work;
   if (persistent_cus > 0) {
     int occ = 0;
     hipError_t e = resident_per_cu(reinterpret_cast<const void*>(kern), block, &occ);
     if (e != hipSuccess) return e;
+    if (per_cu_cap > 0) occ = std::min(occ, per_cu_cap);
     grid = std::min<int64_t>(grid, int64_t(persistent_cus) * occ);
   }
   grid = cap_grid(grid, block);
   std::tuple<P...> args(a...);
   return launch_tuple(kern, dim3(static_cast<uint32_t>(grid)), dim3(block), s, args,
                       std::index_sequence_for<P...>{});
+}
+
+template <typename... P, typename... A>
+hipError_t go(void (*kern)(P...), int block, int64_t work, int persistent_cus, hipStream_t s,
+              A... a) {
+  return go_capped(kern, block, work, persistent_cus, 0, s, a...);
 }
 
 template <class D, int N>
@@ -74,13 +81,13 @@ hipError_t fused_n(const Launch& L, const FusedArgs& a, hipStream_t s) {
   // wide rows: persistent grid on the CU limit, else on the whole chip
   const int grid_cus = L.cu_limit > 0 ? L.cu_limit : L.device_cus;
 #define TW_ROWS(KK)                                                                            \
-  (L.waves <= 4   ? go(twk::fused_rows_kernel<D, N, KK, 4>, block, work_rows, grid_cus, s, a.pp,  \
+  (L.waves <= 4   ? go_capped(twk::fused_rows_kernel<D, N, KK, 4>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp,  \
                        a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps)                                                                   \
-   : L.waves <= 8 ? go(twk::fused_rows_kernel<D, N, KK, 8>, block, work_rows, grid_cus, s, a.pp,  \
+   : L.waves <= 8 ? go_capped(twk::fused_rows_kernel<D, N, KK, 8>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp,  \
                        a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps)                                                                   \
-                  : go(twk::fused_rows_kernel<D, N, KK, 16>, block, work_rows, grid_cus, s, a.pp, \
+                  : go_capped(twk::fused_rows_kernel<D, N, KK, 16>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp, \
                        a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps))
   switch (L.k) {

@@ -15,6 +15,7 @@ thread_local char g_err[512] = {0};
 
 std::atomic<int> g_override_waves{0};
 std::atomic<int> g_override_k{0};
+std::atomic<int> g_wgs_per_cu{0};
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi)
@@ -151,15 +152,11 @@ tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_l
 }
 
 // Register-fit table of the wide-row kernels, generated at build time from the
-// compiler's resource remarks (see build.py): which chunk counts K run without
-// scratch for each (dtype, n, launch bound).
+// compiler's resource remarks (reduce_residual_add_amd/build.py): which chunk
+// counts K run without scratch for each (dtype, n, launch bound).
 #include "twnorm_fit_table.inc"
 
 static const int kAllowedK[] = {1, 2, 3, 4, 6, 8};
-// Among spill-free shapes with the fewest idle chunk slots, this order of K
-// breaks ties (measured on MI355X: fewer, wider wavefronts per row lose
-// latency hiding; more chunk slots per lane cost registers).
-static const int kPreferK[] = {2, 1, 4, 3, 6, 8};
 
 static int k_index(int k) {
   for (int i = 0; i < 6; ++i)
@@ -176,12 +173,28 @@ bool shape_spills(tw_dtype dtype, int n, int waves, int k) {
   return ((kFitMask[dt][n][bucket_of(waves)] >> ki) & 1) == 0;
 }
 
-// Automatic shape: rows of at most 32 chunks go to the narrow-row kernel with
-// the smallest power-of-two team that covers them.  Wider rows take, for each
-// K, the fewest wavefronts W <= 16 that cover the row; among the (W, K) whose
-// kernel spills nothing, the fewest idle chunk slots win, ties broken by
-// kPreferK.  If every candidate spills (very wide rows with many partials),
-// the fewest idle slots win regardless.
+// Shapes measured fastest on MI355X (HBM-resident inputs, shapes swept over
+// waves x chunk slots) for row widths used in practice.
+struct TunedShape {
+  int elem_bytes;
+  int64_t chunks;
+  int n_lo, n_hi;
+  int waves, k;
+};
+static const TunedShape kTuned[] = {
+    {2, 1024, 5, 16, 4, 4},  // 8192 bf16 features, many partials
+    {2, 512, 1, 3, 2, 4},    // 4096 bf16 features, few partials
+    {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
+};
+
+// Automatic shape:
+//  * rows of at most 32 chunks: narrow-row kernel, smallest power-of-two team;
+//  * a measured shape for this (width, n) if it spills nothing;
+//  * else 4 wavefronts with the fewest chunk slots per lane that cover the
+//    row, if that spills nothing;
+//  * else, for each K the fewest wavefronts W <= 16 that cover the row, and
+//    among the spill-free (W, K) the fewest idle chunk slots (ties: smaller
+//    K); if every candidate spills, the fewest idle slots regardless.
 tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
   const int b = elem_bytes(dtype);
   if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
@@ -201,9 +214,25 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
     *shape = Shape{0, 0, team};
     return TW_OK;
   }
+  for (const TunedShape& t : kTuned) {
+    if (t.elem_bytes == b && t.chunks == chunks && n >= t.n_lo && n <= t.n_hi &&
+        !shape_spills(dtype, n, t.waves, t.k)) {
+      *shape = Shape{t.waves, t.k, 0};
+      return TW_OK;
+    }
+  }
+  for (int k : kAllowedK) {
+    if (4 * 64 * k >= chunks) {
+      if (!shape_spills(dtype, n, 4, k)) {
+        *shape = Shape{4, k, 0};
+        return TW_OK;
+      }
+      break;
+    }
+  }
   int best_w = 0, best_k = 0, any_w = 0, any_k = 0;
   int64_t best_waste = -1, any_waste = -1;
-  for (int k : kPreferK) {
+  for (int k : kAllowedK) {
     const int64_t w = (chunks + 64 * k - 1) / (64 * k);
     if (w > 16) continue;
     const int64_t waste = w * 64 * k - chunks;
@@ -223,15 +252,19 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
   return TW_OK;
 }
 
-tw_status set_override(int waves, int k) {
+tw_status set_override(int waves, int k, int wgs_per_cu) {
   bool k_ok = (k == 0);
   for (int a : kAllowedK) k_ok = k_ok || (a == k);
-  if (waves < 0 || waves > 16 || !k_ok || ((waves == 0) != (k == 0)))
-    return fail(TW_ERR_INVALID_ARG, "invalid forced shape (%d waves, %d chunks per lane)", waves, k);
+  if (waves < 0 || waves > 16 || !k_ok || ((waves == 0) != (k == 0)) || wgs_per_cu < 0)
+    return fail(TW_ERR_INVALID_ARG, "invalid forced shape (%d waves, %d chunks per lane, %d per CU)",
+                waves, k, wgs_per_cu);
   g_override_waves.store(waves);
   g_override_k.store(k);
+  g_wgs_per_cu.store(wgs_per_cu);
   return TW_OK;
 }
+
+int wgs_per_cu_cap() { return g_wgs_per_cu.load(); }
 
 }  // namespace twv
 
@@ -255,9 +288,9 @@ const char* tw_last_error(void) { return twv::last_error(); }
 
 int tw_abi_version(void) { return TW_ABI_VERSION; }
 
-tw_status tw_set_fused_shape(int waves, int chunks_per_lane) {
+tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu) {
   twv::clear_error();
-  return twv::set_override(waves, chunks_per_lane);
+  return twv::set_override(waves, chunks_per_lane, wgs_per_cu);
 }
 
 tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves,

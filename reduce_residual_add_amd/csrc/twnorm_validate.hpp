@@ -39,7 +39,9 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape);
 // (from the build's register-fit table).
 bool shape_spills(tw_dtype dtype, int n, int waves, int k);
 
-// Force (waves, k) for wide rows; (0, 0) restores the automatic choice.
-tw_status set_override(int waves, int k);
+// Force (waves, k) for wide rows ((0, 0) restores the automatic choice) and
+// cap the persistent grid at wgs_per_cu workgroups per CU (0 = no cap).
+tw_status set_override(int waves, int k, int wgs_per_cu);
+int wgs_per_cu_cap();
 
 }  // namespace twv
