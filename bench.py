@@ -280,8 +280,11 @@ def main(argv=None):
     gbs = bytes_call / (ms * 1e-3) / 1e9
     rows_per_s = w.rows / (ms * 1e-3)
 
+    metric = METRIC if w.name == "shard70b" else (
+        f"fused reduce+RMSNorm HBM GB/s (% of peak) and token-rows/s, {w.name} workload "
+        f"(H={w.hidden}, N={w.n}, {w.rows} rows)")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
