@@ -244,6 +244,28 @@ def measure_unfused(twn, w, sets, steps, warmup):
     return time_steps([pair(d) for d in sets], steps, warmup)
 
 
+def measure_allgather(twn, w, sets, steps, warmup):
+    """The fused step with the AllGather store: each call writes its rows
+    into N gather buffers of N * rows rows (one per simulated rank), at the
+    offset of the shard it plays (cycling over the N shards)."""
+    import torch
+    ranks = w.n
+    total = ranks * w.rows
+    gathers = [torch.empty((total, w.hidden), dtype=sets[0]["res"].dtype, device="cuda")
+               for _ in range(ranks)]
+    fns = []
+    for i in range(len(sets) * ranks):
+        d = sets[i % len(sets)]
+        off = (i % ranks) * w.rows
+        fns.append(lambda d=d, off=off: twn.fused_reduce_rmsnorm_allgather(
+            d["parts"], d["res"], d["w"], w.eps, gathers, off, residual_out=d["res_out"]))
+    ms, _ = time_steps(fns, steps, warmup)
+    b = w.elem_bytes
+    nbytes = (w.n + 2 + ranks) * w.rows * w.hidden * b + w.hidden * b
+    del gathers
+    return ms, nbytes
+
+
 def measure_copy(twn, total_bytes, steps, warmup):
     import torch
     n = total_bytes // 2
@@ -338,6 +360,9 @@ def main(argv=None):
         rep["unfused_pair"] = {"ms_per_step": ums, "algorithmic_bytes": w.unfused_bytes(),
                                "gbs_on_unfused_bytes": w.unfused_bytes() / (ums * 1e-3) / 1e9,
                                "speedup_fused_vs_unfused": ums / ms}
+        ams, abytes = measure_allgather(twn, w, sets, max(50, args.steps // 4), 10)
+        rep["allgather_store"] = {"ms_per_step": ams, "algorithmic_bytes": abytes,
+                                  "gather_buffers": w.n, "gbs": abytes / (ams * 1e-3) / 1e9}
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
         rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes,
                                "gbs": 2 * cbytes / (cms * 1e-3) / 1e9}

@@ -108,6 +108,30 @@ tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int n, int64_t ro
                                   void* residual_out, int n_cu_limit, void* stream);
 
 /*
+ * Fused path with the AllGather store: the same computation as
+ * tw_fused_reduce_rmsnorm, with the normalised rows written into each of n_ag
+ * gather buffers at rows [ag_row_offset, ag_row_offset + rows) instead of one
+ * `out` ([TW] §3.4: every rank ends with the full normalised sequence; §5: the
+ * fused kernel stores its result straight into the AllGather targets).  On one
+ * GPU the n_ag local buffers stand for the ranks' gather buffers; running the
+ * N token shards (offsets r * rows) fills every buffer with all T rows.
+ *   ag_outs        host array of n_ag device pointers, each a row-major
+ *                  [ag_total_rows, hidden] buffer of `dtype`
+ *   n_ag           1..TW_MAX_PARTIALS
+ *   ag_row_offset  first gather-buffer row this shard writes
+ *   ag_total_rows  rows of each gather buffer; ag_row_offset + rows must fit
+ * Rows outside [ag_row_offset, ag_row_offset + rows) are not touched.
+ * Alias rules: the gather buffers (whole) are pairwise disjoint and overlap no
+ * input and not residual_out; residual_out as in tw_fused_reduce_rmsnorm.
+ */
+tw_status tw_fused_reduce_rmsnorm_allgather(const void* const* partials, int n, int64_t rows,
+                                            int64_t hidden, tw_dtype dtype, const void* residual,
+                                            const void* weight, float eps, void* const* ag_outs,
+                                            int n_ag, int64_t ag_row_offset,
+                                            int64_t ag_total_rows, void* residual_out,
+                                            int n_cu_limit, void* stream);
+
+/*
  * Unfused comparison path, first half: reduced = round(sum_i partials[i]),
  * the reduce of a ReduceScatter written to HBM ([TW] §4: the intermediate
  * makes a round trip through HBM).  `reduced` may be exactly one of the

@@ -42,7 +42,8 @@ _STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
                  TW_ERR_UNSUPPORTED: "TW_ERR_UNSUPPORTED", TW_ERR_ALIAS: "TW_ERR_ALIAS",
                  TW_ERR_HIP: "TW_ERR_HIP"}
 
-EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_reduce", "tw_rmsnorm", "tw_stream_copy",
+EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_fused_reduce_rmsnorm_allgather", "tw_reduce",
+            "tw_rmsnorm", "tw_stream_copy",
             "tw_cu_masked_stream",
             "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
             "tw_last_error", "tw_abi_version")
@@ -60,6 +61,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_fused_reduce_rmsnorm.argtypes = [_c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp,
                                             _vp, _c.c_float, _vp, _vp, _c.c_int, _vp]
     lib.tw_fused_reduce_rmsnorm.restype = _c.c_int
+    lib.tw_fused_reduce_rmsnorm_allgather.argtypes = [
+        _c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp, _vp, _c.c_float, _c.POINTER(_vp),
+        _c.c_int, _i64, _i64, _vp, _c.c_int, _vp]
+    lib.tw_fused_reduce_rmsnorm_allgather.restype = _c.c_int
     lib.tw_reduce.argtypes = [_c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp, _c.c_int, _vp]
     lib.tw_reduce.restype = _c.c_int
     lib.tw_rmsnorm.argtypes = [_vp, _i64, _i64, _c.c_int, _vp, _vp, _c.c_float, _vp, _vp,
@@ -174,6 +179,40 @@ def fused_reduce_rmsnorm(partials: Sequence, residual, weight, eps: float, *, ou
                                        out.data_ptr(), residual_out.data_ptr(), int(n_cu_limit),
                                        _stream_ptr(stream)))
     return out, residual_out
+
+
+def fused_reduce_rmsnorm_allgather(partials: Sequence, residual, weight, eps: float,
+                                   ag_outs: Sequence, ag_row_offset: int, *, residual_out=None,
+                                   n_cu_limit: int = 0, stream=None):
+    """Fused step with the AllGather store: the normalised rows go to rows
+    [ag_row_offset, ag_row_offset + rows) of every buffer in `ag_outs`
+    (each [T, hidden]).  Returns residual_out."""
+    torch = _torch()
+    lib = load()
+    rows, hidden = _rows_hidden(residual)
+    dt, dev = residual.dtype, residual.device
+    n, n_ag = len(partials), len(ag_outs)
+    if n < 1 or n > TW_MAX_PARTIALS or n_ag < 1 or n_ag > TW_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TW_MAX_PARTIALS} partials and gather buffers")
+    for i, p in enumerate(partials):
+        _check_tensor(p, f"partials[{i}]", (rows, hidden), dt, dev)
+    _check_tensor(residual, "residual", (rows, hidden), dt, dev)
+    _check_tensor(weight, "weight", (hidden,), dt, dev)
+    total = int(ag_outs[0].shape[0])
+    for j, g in enumerate(ag_outs):
+        _check_tensor(g, f"ag_outs[{j}]", (total, hidden), dt, dev)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    if rows == 0:
+        return residual_out
+    arr = (_vp * n)(*[p.data_ptr() for p in partials])
+    ag = (_vp * n_ag)(*[g.data_ptr() for g in ag_outs])
+    _check(lib.tw_fused_reduce_rmsnorm_allgather(
+        arr, n, rows, hidden, dtype_code(residual), residual.data_ptr(), weight.data_ptr(),
+        float(eps), ag, n_ag, int(ag_row_offset), total, residual_out.data_ptr(), int(n_cu_limit),
+        _stream_ptr(stream)))
+    return residual_out
 
 
 def reduce(partials: Sequence, *, out=None, n_cu_limit: int = 0, stream=None):

@@ -147,15 +147,15 @@ tw_status run(int n_cu_limit, hipStream_t caller, const char* what, F&& launch) 
   return le == hipSuccess ? TW_OK : hip_fail(le, what);
 }
 
-tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t hidden,
-                     tw_dtype dtype, const void* residual, const void* weight, float eps,
-                     void* out, void* residual_out, int n_cu_limit, void* stream) {
-  tw_status st = twv::check_fused(partials, n, rows, hidden, dtype, residual, weight, eps, out,
-                                  residual_out, n_cu_limit);
-  if (st != TW_OK) return st;
+// Everything after validation: shape, device, launch.  `outs` holds the
+// destinations of the normalised rows (one buffer for the plain call).
+tw_status fused_launch(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                       tw_dtype dtype, const void* residual, const void* weight, float eps,
+                       const twk::OutPtrs& outs, void* residual_out, int n_cu_limit,
+                       void* stream) {
   if (rows == 0) return TW_OK;
   twv::Shape sh{};
-  st = twv::choose_shape(dtype, hidden, n, &sh);
+  tw_status st = twv::choose_shape(dtype, hidden, n, &sh);
   if (st != TW_OK) return st;
   int cus = 0;
   st = current_device_cus(&cus);
@@ -165,7 +165,7 @@ tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t h
   for (int i = 0; i < n; ++i) a.pp.p[i] = static_cast<const twk::u32x4*>(partials[i]);
   a.residual = static_cast<const twk::u32x4*>(residual);
   a.weight = static_cast<const twk::u32x4*>(weight);
-  a.out = static_cast<twk::u32x4*>(out);
+  a.outs = outs;
   a.residual_out = static_cast<twk::u32x4*>(residual_out);
   a.rows = rows;
   a.chunks = static_cast<int>(hidden * twv::elem_bytes(dtype) / 16);
@@ -179,6 +179,20 @@ tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t h
              });
 }
 
+tw_status fused_impl(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                     tw_dtype dtype, const void* residual, const void* weight, float eps,
+                     void* out, void* residual_out, int n_cu_limit, void* stream) {
+  tw_status st = twv::check_fused(partials, n, rows, hidden, dtype, residual, weight, eps, out,
+                                  residual_out, n_cu_limit);
+  if (st != TW_OK) return st;
+  twk::OutPtrs outs{};
+  outs.p[0] = static_cast<twk::u32x4*>(out);
+  outs.n = 1;
+  outs.row0 = 0;
+  return fused_launch(partials, n, rows, hidden, dtype, residual, weight, eps, outs, residual_out,
+                      n_cu_limit, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +204,25 @@ tw_status tw_fused_reduce_rmsnorm(const void* const* partials, int n, int64_t ro
   twv::clear_error();
   return fused_impl(partials, n, rows, hidden, dtype, residual, weight, eps, out, residual_out,
                     n_cu_limit, stream);
+}
+
+tw_status tw_fused_reduce_rmsnorm_allgather(const void* const* partials, int n, int64_t rows,
+                                            int64_t hidden, tw_dtype dtype, const void* residual,
+                                            const void* weight, float eps, void* const* ag_outs,
+                                            int n_ag, int64_t ag_row_offset,
+                                            int64_t ag_total_rows, void* residual_out,
+                                            int n_cu_limit, void* stream) {
+  twv::clear_error();
+  tw_status st = twv::check_fused_allgather(partials, n, rows, hidden, dtype, residual, weight,
+                                            eps, ag_outs, n_ag, ag_row_offset, ag_total_rows,
+                                            residual_out, n_cu_limit);
+  if (st != TW_OK) return st;
+  twk::OutPtrs outs{};
+  for (int j = 0; j < n_ag; ++j) outs.p[j] = static_cast<twk::u32x4*>(ag_outs[j]);
+  outs.n = n_ag;
+  outs.row0 = ag_row_offset;
+  return fused_launch(partials, n, rows, hidden, dtype, residual, weight, eps, outs, residual_out,
+                      n_cu_limit, stream);
 }
 
 tw_status tw_rmsnorm(const void* reduced, int64_t rows, int64_t hidden, tw_dtype dtype,

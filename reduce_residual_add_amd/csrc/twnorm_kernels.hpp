@@ -37,6 +37,16 @@ struct PartialPtrs {
   const u32x4* p[kMaxPartials];
 };
 
+// Destinations of the normalised output: `n` buffers, each written at row
+// `row0 + row` (one buffer at row 0 for the plain fused call; one per rank's
+// AllGather buffer for the all-gather store).
+constexpr int kMaxOutputs = 16;
+struct OutPtrs {
+  u32x4* p[kMaxOutputs];
+  int n;
+  int64_t row0;
+};
+
 // Storage formats.  A 16-byte chunk holds kElems values.
 struct Bf16 {
   static constexpr int kElems = 8;
@@ -232,8 +242,8 @@ __device__ __forceinline__ void load_row(u32x4 (&raw)[K][N + 1], const PartialPt
 template <class D, int N, int K, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
 fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
-                  const u32x4* __restrict__ weight, u32x4* __restrict__ out,
-                  u32x4* residual_out, int64_t rows, int chunks, float hidden_f, float eps) {
+                  const u32x4* __restrict__ weight, OutPtrs outs, u32x4* residual_out,
+                  int64_t rows, int chunks, float hidden_f, float eps) {
   constexpr int E = D::kElems;
   __shared__ float red[2][MAXW];
   const int tid = threadIdx.x;
@@ -256,7 +266,6 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
   for (; row < rows; row += gridDim.x) {
     const int64_t base = row * chunks;
     const rsrc_t ro_rsrc = make_rsrc(residual_out + base, row_bytes);
-    const rsrc_t o_rsrc = make_rsrc(out + base, row_bytes);
     // Slots past the row's end loaded zeros, so they add nothing to ss, and
     // their stores fall outside the descriptor's range and are dropped.
     float x[K][E];
@@ -283,9 +292,15 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
       parity ^= 1;
     }
     const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
+    u32x4 o[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      buf_store(scale_chunk<D>(x[k], inv, wv[k]), o_rsrc, lane_off + k * slot_stride);
+    for (int k = 0; k < K; ++k) o[k] = scale_chunk<D>(x[k], inv, wv[k]);
+    const int64_t obase = (outs.row0 + row) * chunks;
+    for (int j = 0; j < outs.n; ++j) {
+      const rsrc_t o_rsrc = make_rsrc(outs.p[j] + obase, row_bytes);
+#pragma unroll
+      for (int k = 0; k < K; ++k) buf_store(o[k], o_rsrc, lane_off + k * slot_stride);
+    }
   }
 }
 
@@ -298,9 +313,8 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 template <class D, int N>
 __global__ void __launch_bounds__(256)
 fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
-                  const u32x4* __restrict__ weight, u32x4* __restrict__ out,
-                  u32x4* residual_out, int64_t rows, int chunks, int team, float hidden_f,
-                  float eps) {
+                  const u32x4* __restrict__ weight, OutPtrs outs, u32x4* residual_out,
+                  int64_t rows, int chunks, int team, float hidden_f, float eps) {
   constexpr int E = D::kElems;
   const int tid = threadIdx.x;
   const int rows_per_block = blockDim.x / team;
@@ -327,7 +341,11 @@ fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
     }
     ss = team_sum(ss, team);
     const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
-    if (act) st_stream(out + off, scale_chunk<D>(x, inv, wv));
+    if (act) {
+      const u32x4 o = scale_chunk<D>(x, inv, wv);
+      const int64_t ooff = (outs.row0 + row) * chunks + c;
+      for (int j = 0; j < outs.n; ++j) st_stream(outs.p[j] + ooff, o);
+    }
   }
 }
 

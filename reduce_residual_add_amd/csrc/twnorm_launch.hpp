@@ -13,7 +13,7 @@ struct FusedArgs {
   twk::PartialPtrs pp;
   const twk::u32x4* residual;
   const twk::u32x4* weight;
-  twk::u32x4* out;
+  twk::OutPtrs outs;
   twk::u32x4* residual_out;
   int64_t rows;
   int chunks;      // 16-byte chunks per row

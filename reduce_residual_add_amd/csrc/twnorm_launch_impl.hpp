@@ -82,19 +82,19 @@ hipError_t fused_n(const Launch& L, const FusedArgs& a, hipStream_t s) {
   const int grid_cus = L.cu_limit > 0 ? L.cu_limit : L.device_cus;
 #define TW_ROWS(KK)                                                                            \
   (L.waves <= 4   ? go_capped(twk::fused_rows_kernel<D, N, KK, 4>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp,  \
-                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.residual, a.weight, a.outs, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps)                                                                   \
    : L.waves <= 8 ? go_capped(twk::fused_rows_kernel<D, N, KK, 8>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp,  \
-                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.residual, a.weight, a.outs, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps)                                                                   \
                   : go_capped(twk::fused_rows_kernel<D, N, KK, 16>, block, work_rows, grid_cus, L.wgs_per_cu, s, a.pp, \
-                       a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks, a.hidden_f, \
+                       a.residual, a.weight, a.outs, a.residual_out, a.rows, a.chunks, a.hidden_f, \
                        a.eps))
   switch (L.k) {
     case 0: {
       const int rows_per_block = 256 / L.team;
       return go(twk::fused_team_kernel<D, N>, 256, (a.rows + rows_per_block - 1) / rows_per_block,
-                L.cu_limit, s, a.pp, a.residual, a.weight, a.out, a.residual_out, a.rows, a.chunks,
+                L.cu_limit, s, a.pp, a.residual, a.weight, a.outs, a.residual_out, a.rows, a.chunks,
                 L.team, a.hidden_f, a.eps);
     }
     case 1: return TW_ROWS(1);

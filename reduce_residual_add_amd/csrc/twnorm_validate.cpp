@@ -84,40 +84,100 @@ void clear_error() { g_err[0] = '\0'; }
 
 const char* last_error() { return g_err; }
 
-tw_status check_fused(const void* const* partials, int n, int64_t rows, int64_t hidden,
-                      tw_dtype dtype, const void* residual, const void* weight, float eps,
-                      const void* out, const void* residual_out, int n_cu_limit) {
+// Inputs and residual_out of the fused paths; sets the bytes of one
+// [rows, hidden] tensor.
+static tw_status check_fused_inputs(const void* const* partials, int n, int64_t rows,
+                                    int64_t hidden, tw_dtype dtype, const void* residual,
+                                    const void* weight, float eps, const void* residual_out,
+                                    int n_cu_limit, int64_t* tensor_bytes) {
   tw_status st = check_partials(partials, n);
   if (st != TW_OK) return st;
   if (residual == nullptr) return fail(TW_ERR_INVALID_ARG, "residual is NULL");
   if (weight == nullptr) return fail(TW_ERR_INVALID_ARG, "weight is NULL");
-  if (out == nullptr) return fail(TW_ERR_INVALID_ARG, "out is NULL");
   if (residual_out == nullptr) return fail(TW_ERR_INVALID_ARG, "residual_out is NULL");
   if (!(eps >= 0.0f) || std::isinf(eps))
     return fail(TW_ERR_INVALID_ARG, "eps must be finite and >= 0 (got %g)", (double)eps);
-  int64_t tb = 0;
-  st = check_shape(rows, hidden, dtype, n_cu_limit, &tb);
+  st = check_shape(rows, hidden, dtype, n_cu_limit, tensor_bytes);
   if (st != TW_OK) return st;
   for (int i = 0; i < n; ++i)
     if (misaligned(partials[i]))
       return fail(TW_ERR_UNSUPPORTED, "partials[%d] is not 16-byte aligned", i);
-  if (misaligned(residual) || misaligned(weight) || misaligned(out) || misaligned(residual_out))
+  if (misaligned(residual) || misaligned(weight) || misaligned(residual_out))
     return fail(TW_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
-
-  const int64_t wb = hidden * elem_bytes(dtype);
-  const Span s_out = span(out, tb), s_res = span(residual, tb), s_rout = span(residual_out, tb),
-             s_w = span(weight, wb);
-  for (int i = 0; i < n; ++i) {
-    const Span s_p = span(partials[i], tb);
-    if (overlap(s_out, s_p)) return fail(TW_ERR_ALIAS, "out overlaps partials[%d]", i);
-    if (overlap(s_rout, s_p)) return fail(TW_ERR_ALIAS, "residual_out overlaps partials[%d]", i);
-  }
-  if (overlap(s_out, s_res)) return fail(TW_ERR_ALIAS, "out overlaps residual");
-  if (overlap(s_out, s_w)) return fail(TW_ERR_ALIAS, "out overlaps weight");
-  if (overlap(s_out, s_rout)) return fail(TW_ERR_ALIAS, "out overlaps residual_out");
+  const int64_t tb = *tensor_bytes;
+  const Span s_res = span(residual, tb), s_rout = span(residual_out, tb),
+             s_w = span(weight, hidden * elem_bytes(dtype));
+  for (int i = 0; i < n; ++i)
+    if (overlap(s_rout, span(partials[i], tb)))
+      return fail(TW_ERR_ALIAS, "residual_out overlaps partials[%d]", i);
   if (overlap(s_rout, s_w)) return fail(TW_ERR_ALIAS, "residual_out overlaps weight");
   if (residual_out != residual && overlap(s_rout, s_res))
     return fail(TW_ERR_ALIAS, "residual_out partially overlaps residual");
+  return TW_OK;
+}
+
+// An output span may overlap no input, residual_out or other output.
+static tw_status check_output_span(const char* name, Span s_o, const void* const* partials, int n,
+                                   int64_t tb, const void* residual, const void* weight,
+                                   int64_t wb, const void* residual_out) {
+  for (int i = 0; i < n; ++i)
+    if (overlap(s_o, span(partials[i], tb)))
+      return fail(TW_ERR_ALIAS, "%s overlaps partials[%d]", name, i);
+  if (overlap(s_o, span(residual, tb))) return fail(TW_ERR_ALIAS, "%s overlaps residual", name);
+  if (overlap(s_o, span(weight, wb))) return fail(TW_ERR_ALIAS, "%s overlaps weight", name);
+  if (overlap(s_o, span(residual_out, tb)))
+    return fail(TW_ERR_ALIAS, "%s overlaps residual_out", name);
+  return TW_OK;
+}
+
+tw_status check_fused(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                      tw_dtype dtype, const void* residual, const void* weight, float eps,
+                      const void* out, const void* residual_out, int n_cu_limit) {
+  if (out == nullptr) return fail(TW_ERR_INVALID_ARG, "out is NULL");
+  int64_t tb = 0;
+  tw_status st = check_fused_inputs(partials, n, rows, hidden, dtype, residual, weight, eps,
+                                    residual_out, n_cu_limit, &tb);
+  if (st != TW_OK) return st;
+  if (misaligned(out)) return fail(TW_ERR_UNSUPPORTED, "out is not 16-byte aligned");
+  return check_output_span("out", span(out, tb), partials, n, tb, residual, weight,
+                           hidden * elem_bytes(dtype), residual_out);
+}
+
+tw_status check_fused_allgather(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                                tw_dtype dtype, const void* residual, const void* weight,
+                                float eps, const void* const* ag_outs, int n_ag,
+                                int64_t ag_row_offset, int64_t ag_total_rows,
+                                const void* residual_out, int n_cu_limit) {
+  if (ag_outs == nullptr) return fail(TW_ERR_INVALID_ARG, "ag_outs array is NULL");
+  if (n_ag < 1 || n_ag > TW_MAX_PARTIALS)
+    return fail(TW_ERR_INVALID_ARG, "n_ag must be in [1, %d] (got %d)", TW_MAX_PARTIALS, n_ag);
+  for (int j = 0; j < n_ag; ++j)
+    if (ag_outs[j] == nullptr) return fail(TW_ERR_INVALID_ARG, "ag_outs[%d] is NULL", j);
+  if (ag_row_offset < 0) return fail(TW_ERR_INVALID_ARG, "ag_row_offset must be >= 0");
+  int64_t tb = 0;
+  tw_status st = check_fused_inputs(partials, n, rows, hidden, dtype, residual, weight, eps,
+                                    residual_out, n_cu_limit, &tb);
+  if (st != TW_OK) return st;
+  if (ag_total_rows < 0 || ag_row_offset > ag_total_rows - rows)
+    return fail(TW_ERR_INVALID_ARG, "rows [%lld, %lld) do not fit the %lld-row gather buffers",
+                (long long)ag_row_offset, (long long)(ag_row_offset + rows),
+                (long long)ag_total_rows);
+  const int64_t row_bytes = hidden * elem_bytes(dtype);
+  if (ag_total_rows > INT64_MAX / row_bytes)
+    return fail(TW_ERR_INVALID_ARG, "gather buffer size overflows 64-bit byte counts");
+  const int64_t gb = ag_total_rows * row_bytes;
+  char name[32];
+  for (int j = 0; j < n_ag; ++j) {
+    if (misaligned(ag_outs[j]))
+      return fail(TW_ERR_UNSUPPORTED, "ag_outs[%d] is not 16-byte aligned", j);
+    snprintf(name, sizeof(name), "ag_outs[%d]", j);
+    st = check_output_span(name, span(ag_outs[j], gb), partials, n, tb, residual, weight,
+                           row_bytes, residual_out);
+    if (st != TW_OK) return st;
+    for (int i = 0; i < j; ++i)
+      if (overlap(span(ag_outs[j], gb), span(ag_outs[i], gb)))
+        return fail(TW_ERR_ALIAS, "ag_outs[%d] overlaps ag_outs[%d]", j, i);
+  }
   return TW_OK;
 }
 

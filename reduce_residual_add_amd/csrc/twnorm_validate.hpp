@@ -28,6 +28,11 @@ const char* last_error();
 tw_status check_fused(const void* const* partials, int n, int64_t rows, int64_t hidden,
                       tw_dtype dtype, const void* residual, const void* weight, float eps,
                       const void* out, const void* residual_out, int n_cu_limit);
+tw_status check_fused_allgather(const void* const* partials, int n, int64_t rows, int64_t hidden,
+                                tw_dtype dtype, const void* residual, const void* weight,
+                                float eps, const void* const* ag_outs, int n_ag,
+                                int64_t ag_row_offset, int64_t ag_total_rows,
+                                const void* residual_out, int n_cu_limit);
 tw_status check_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
                        tw_dtype dtype, const void* reduced, int n_cu_limit);
 tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_limit);

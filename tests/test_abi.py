@@ -149,6 +149,37 @@ def test_reduce_rmsnorm_copy_validation(lib):
     assert lib.tw_stream_copy(b.parts[0], b.parts[1], 0, 0, None) == OK
 
 
+def test_allgather_validation(lib):
+    b = Bufs()
+    tensor = b.rows * b.hidden * 2
+    base = 0x7F0000000000 + 2048 * MB
+    ag = [base + j * 64 * MB for j in range(4)]
+
+    def call(ag_list=ag, n_ag=None, off=0, total=16, rows=b.rows, res_out=b.res_out, **kw):
+        parts = (ctypes.c_void_p * 2)(*b.parts)
+        arr = None if ag_list is None else (ctypes.c_void_p * max(1, len(ag_list)))(*ag_list)
+        if n_ag is None:
+            n_ag = 1 if ag_list is None else len(ag_list)
+        return lib.tw_fused_reduce_rmsnorm_allgather(parts, 2, rows, b.hidden, BF16, b.residual,
+                                                     b.weight, 1e-5, arr, n_ag, off, total,
+                                                     res_out, 0, None)
+    assert call(ag_list=None) == INV
+    assert call(n_ag=0) == INV
+    assert call(n_ag=17, ag_list=ag * 5) == INV
+    assert call(ag_list=[ag[0], None]) == INV
+    assert call(off=-1) == INV
+    assert call(off=13, total=16) == INV              # 13 + 4 rows > 16
+    assert call(off=0, total=3) == INV
+    assert call(ag_list=[ag[0] + 8]) == UNS
+    assert call(ag_list=[ag[0], ag[0] + 1024]) == ALIAS   # second starts inside the first (2 KiB)
+    assert call(ag_list=[b.parts[1]]) == ALIAS
+    assert call(ag_list=[b.residual - 16 * 64 * 2 + tensor]) == ALIAS
+    assert call(ag_list=[b.weight]) == ALIAS
+    assert call(ag_list=[b.res_out]) == ALIAS
+    assert call(rows=0) == OK                       # validated no-op
+    assert call(rows=0, off=12, total=12) == OK
+
+
 def test_masked_stream_argument_checks(lib):
     h = ctypes.c_void_p()
     assert lib.tw_cu_masked_stream(8, None) == INV

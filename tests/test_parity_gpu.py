@@ -306,3 +306,58 @@ def test_fourth_cu_limit_is_refused(twn):
     twn.fused_reduce_rmsnorm(parts, res, wt, 1e-5, out=out, n_cu_limit=16)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(out)) > 0
+
+
+# ---------------------------------------------------------------------------
+# AllGather store: every rank's shard lands in every rank's gather buffer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,ranks", [("page1", 2), ("shard70b", 8), ("tiny", 2)])
+def test_allgather_store_simulated_ranks(twn, name, ranks):
+    """Token-boundary ReduceScatter -> add + norm -> AllGather on `ranks`
+    simulated ranks: rank r owns rows [r*R, (r+1)*R) of the T-token sequence,
+    reads only its rows of the partials and residual, and writes its
+    normalised rows into all `ranks` gather buffers.  Afterwards every gather
+    buffer holds the full normalised sequence, identical to normalising all T
+    rows at once ("TokenWeave 策略详解", §3.2-§3.4)."""
+    import torch
+    w = workloads.get(name)
+    rows_per_rank = min(w.rows, 256)
+    T = rows_per_rank * ranks
+    _say(f"[allgather] {name} ranks={ranks} T={T}")
+    inp = workloads.make(w, seed=9, rows=T)
+    parts, res, wt = inputs_to_dev(inp)
+    sentinel = 3.0
+    gathers = [torch.full((T, w.hidden), sentinel, dtype=res.dtype, device="cuda") for _ in range(ranks)]
+    res_out = torch.empty_like(res)
+    for r in range(ranks):
+        sl = slice(r * rows_per_rank, (r + 1) * rows_per_rank)
+        twn.fused_reduce_rmsnorm_allgather([p[sl] for p in parts], res[sl], wt, inp["eps"], gathers,
+                                           r * rows_per_rank, residual_out=res_out[sl])
+    torch.cuda.synchronize()
+    g0 = from_dev(gathers[0], w.dtype)
+    for g in gathers[1:]:
+        assert np.array_equal(from_dev(g, w.dtype), g0)
+    ref_out, ref_res = O.fused_from_storage(inp)
+    assert_parity(g0, ref_out, w.dtype, "gathered out")
+    assert_parity(from_dev(res_out, w.dtype), ref_res, w.dtype, "residual_out")
+    # the same rows through the plain fused call give the same bits
+    out_plain, _ = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out_plain, w.dtype), g0)
+
+
+def test_allgather_store_leaves_other_rows(twn):
+    import torch
+    _say("[allgather] partial range")
+    inp = workloads.make_random(3, 5, 8192, "bf16", seed=4)
+    parts, res, wt = inputs_to_dev(inp)
+    T = 16
+    gathers = [torch.full((T, 8192), -2.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    twn.fused_reduce_rmsnorm_allgather(parts, res, wt, 1e-5, gathers, 7)
+    torch.cuda.synchronize()
+    ref_out, _ = O.fused_from_storage(inp)
+    for g in gathers:
+        gh = from_dev(g, "bf16")
+        assert_parity(gh[7:12], ref_out, "bf16", "written rows")
+        untouched = np.concatenate([gh[:7], gh[12:]])
+        assert np.all(untouched == O.bf16_encode_rne(np.array([-2.0]))[0])
