@@ -363,6 +363,17 @@ def main(argv=None):
         ams, abytes = measure_allgather(twn, w, sets, max(50, args.steps // 4), 10)
         rep["allgather_store"] = {"ms_per_step": ams, "algorithmic_bytes": abytes,
                                   "gather_buffers": w.n, "gbs": abytes / (ams * 1e-3) / 1e9}
+        # decode-size rows: latency per call at a few row counts (same shape
+        # as the full workload: the launch shape depends on (dtype, H, N) only)
+        dec = {}
+        for rows in (1, 8, 64):
+            wd = w.with_rows(rows)
+            dsets = make_sets(workloads.make(wd, seed=args.seed), 8)
+            dms, _ = measure_fused(twn, wd, dsets, 0, 400, 40)
+            dec[str(rows)] = {"us_per_call": round(dms * 1e3, 3),
+                              "gbs": round(wd.fused_bytes() / (dms * 1e-3) / 1e9, 1)}
+            del dsets
+        rep["decode_rows"] = dec
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
         rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes,
                                "gbs": 2 * cbytes / (cms * 1e-3) / 1e9}
