@@ -37,11 +37,19 @@ KERNEL_SOURCES = ["reduce_residual_add_amd/csrc/twnorm_kernels.hpp",
                   "reduce_residual_add_amd/csrc/twnorm_validate.cpp"]
 
 
+def _strip_comments(src: str) -> str:
+    """C++ source without comments and whitespace (so that editing comments
+    does not mark the kernel as changed)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "".join(src.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -8,7 +8,8 @@
 // loads and its stores:
 //
 //   loads   N partial chunks + 1 residual chunk per 16-byte chunk slot,
-//           all issued before the first add (memory-level parallelism)
+//           all issued before the first add (memory-level parallelism);
+//           the next row's loads are in flight while this row finishes
 //   sum     s = p_0 + ... + p_{N-1} in index order, x = r + s   (float32)
 //   store   residual_out = round(x)            (the X = X + Y update)
 //   reduce  sum of x^2: per lane -> DPP / ds_swizzle butterfly inside the
@@ -31,7 +32,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxPartials = 16;
-constexpr int kMaxWaves = 16;  // wavefronts per row, wide-row kernel
 
 struct PartialPtrs {
   const u32x4* p[kMaxPartials];
@@ -238,7 +238,7 @@ __device__ __forceinline__ u32x4 scale_chunk(const float* x, float inv, const u3
 // sum of squares is reduced, scaled and stored.  Raw chunks of one row sit
 // in K * (N + 1) * 4 VGPRs, the float32 row in K * E.
 // MAXW sets the launch bound: 4 (256 threads) leaves the compiler up to 512
-// VGPRs per lane, 16 (1024 threads) caps it at 128.
+// VGPRs per lane, 8 (512 threads) up to 256, 16 (1024 threads) caps it at 128.
 // ---------------------------------------------------------------------------
 template <int N, int K>
 __device__ __forceinline__ void load_row(u32x4 (&raw)[K][N + 1], const PartialPtrs& pp,

@@ -361,3 +361,32 @@ def test_allgather_store_leaves_other_rows(twn):
         assert_parity(gh[7:12], ref_out, "bf16", "written rows")
         untouched = np.concatenate([gh[:7], gh[12:]])
         assert np.all(untouched == O.bf16_encode_rne(np.array([-2.0]))[0])
+
+
+def test_many_rows_per_workgroup(twn):
+    """Rows far beyond the resident grid: every workgroup walks tens of rows
+    through the software-pipelined loop (and the narrow-row kernel loops too)."""
+    import torch
+    for n, rows, hidden, dtype in [(3, 20011, 1024, "bf16"), (2, 40000, 64, "f32")]:
+        _say(f"[many rows] n={n} rows={rows} H={hidden} {dtype}")
+        inp = workloads.make_random(n, rows, hidden, dtype, seed=rows)
+        out, res_out = _run_fused(twn, inp)
+        idx = sample_rows(rows, k=512, seed=1)
+        ref_out, ref_res = _oracle_rows(inp, idx)
+        assert_parity(res_out[idx], ref_res, dtype, "residual_out")
+        assert_parity(out[idx], ref_out, dtype, "out")
+
+
+def test_same_partial_twice(twn):
+    """Passing one buffer twice sums it twice (reads may repeat)."""
+    import torch
+    _say("[same partial twice]")
+    inp = workloads.make_random(1, 33, 4096, "bf16", seed=8)
+    parts, res, wt = inputs_to_dev(inp)
+    out, res_out = twn.fused_reduce_rmsnorm([parts[0], parts[0]], res, wt, 1e-5)
+    torch.cuda.synchronize()
+    p = O.decode(inp["partials"][0], "bf16")
+    ref_out, ref_res = O.fused([p, p], O.decode(inp["residual"], "bf16"), O.decode(inp["weight"], "bf16"),
+                               O.eps_as_passed(1e-5))
+    assert_parity(from_dev(res_out, "bf16"), ref_res, "bf16", "residual_out")
+    assert_parity(from_dev(out, "bf16"), ref_out, "bf16", "out")
