@@ -80,6 +80,8 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--report", default="", help="write a detailed JSON report here")
+    p.add_argument("--overlap-cus", type=int, default=32,
+                   help="CUs given to the fused call in the --report two-split overlap")
     p.add_argument("--calibration-copies", type=int, default=0,
                    help="after the timed steps, run this many plain copies of "
                         f"{COPY_CAL_BYTES >> 20} MiB (hardware-counter calibration)")
@@ -274,6 +276,59 @@ def measure_allgather(twn, w, sets, steps, warmup):
     return ms, nbytes
 
 
+def measure_overlap(twn, w, sets, k, iters=40):
+    """Two-split overlap: fused calls for one token split on the first k CUs
+    while the row-parallel GEMM of the other split (the MLP down-projection
+    of an 8-way tensor-parallel 70B-class layer: [rows, 3584] x [3584, H],
+    bf16, hipBLASLt via torch) runs on the other CUs.  Each side queues
+    `iters` calls and joins once, so no per-call cross-queue dependency is
+    timed.  Returns a dict of per-iteration times in microseconds."""
+    import torch
+    a = torch.randn(w.rows, 3584, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(3584, w.hidden, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(w.rows, w.hidden, device="cuda", dtype=torch.bfloat16)
+    masked = twn.cu_masked_stream(k)
+    comp = twn.cu_complement_stream(k)
+    fused = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"],
+                               n_cu_limit=k, stream=masked) for d in sets]
+
+    def gemm():
+        torch.matmul(a, b, out=c)
+
+    def timed(work):   # work() enqueues; returns microseconds per iteration
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        work()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / iters
+
+    def fused_on_masked():
+        for i in range(iters):
+            fused[i % len(fused)]()
+
+    def gemm_on(stream):
+        with torch.cuda.stream(stream):
+            for _ in range(iters):
+                gemm()
+
+    def both():
+        fused_on_masked()
+        gemm_on(comp)
+
+    for f in (fused_on_masked, lambda: gemm_on(comp), lambda: gemm_on(torch.cuda.current_stream())):
+        f()   # warm-up (hipBLASLt heuristics, code objects)
+    res = {
+        "k_cus": k,
+        "gemm_all_cus_us": timed(lambda: gemm_on(torch.cuda.current_stream())),
+        "gemm_on_complement_us": timed(lambda: gemm_on(comp)),
+        "fused_on_k_cus_us": timed(fused_on_masked),
+        "overlapped_us": timed(both),
+    }
+    gflop = 2.0 * w.rows * 3584 * w.hidden / 1e9
+    res["gemm_tflops_all_cus"] = gflop / res["gemm_all_cus_us"] * 1e-3
+    return res
+
+
 def measure_copy(twn, total_bytes, steps, warmup):
     import torch
     n = total_bytes // 2
@@ -382,6 +437,12 @@ def main(argv=None):
                               "gbs": round(wd.fused_bytes() / (dms * 1e-3) / 1e9, 1)}
             del dsets
         rep["decode_rows"] = dec
+        ov = measure_overlap(twn, w, sets, args.overlap_cus)
+        full_fused_us = ms * 1e3
+        ov["fused_all_cus_us"] = full_fused_us
+        ov["sequential_all_cus_us"] = ov["gemm_all_cus_us"] + full_fused_us
+        ov["overlap_speedup_vs_sequential"] = ov["sequential_all_cus_us"] / ov["overlapped_us"]
+        rep["two_split_overlap"] = ov
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
         rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes,
                                "gbs": 2 * cbytes / (cms * 1e-3) / 1e9}

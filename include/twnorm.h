@@ -6,6 +6,8 @@
  * Sources (cited by page title and section):
  *   [TW] "TokenWeave 策略详解：以大模型推理为例" (nanhubrain.csdn.net)
  *   [TP] "张量并行Tensor Parallelism" (scmmm.top)
+ *   [TWS] "TokenWeave: Efficient Compute-Communication Overlap for
+ *         Distributed LLM Inference" (gist.science lay summary)
  *
  * What is computed, per token row t and feature j (float32 arithmetic):
  *   s[t,j]            = p_0[t,j] + p_1[t,j] + ... + p_{n-1}[t,j]   (index order)
@@ -52,9 +54,10 @@
  *              k in [1, CUs) runs the kernel on at most k CUs (persistent grid
  *              on a cached CU-masked stream, ordered after and before `stream`
  *              by events).  Results are bit-identical for every n_cu_limit.
- *              Each distinct k needs a hardware queue of its own for the life
- *              of the process: at most 3 distinct k per device and process;
- *              a fourth returns TW_ERR_UNSUPPORTED.
+ *              Each distinct CU mask needs a hardware queue of its own for the
+ *              life of the process: at most 3 distinct masks (limits k, and
+ *              complements from tw_cu_complement_stream) per device and
+ *              process; a fourth returns TW_ERR_UNSUPPORTED.
  *   Determinism The summation order depends only on (dtype, hidden, n): the
  *              same row gives the same bits whatever rows, shard offset or
  *              n_cu_limit are.
@@ -172,6 +175,15 @@ tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_lim
  * Counts toward the 3 distinct limits a process may use.
  */
 tw_status tw_cu_masked_stream(int n_cu_limit, void** stream);
+
+/*
+ * The library's stream restricted to the CUs that the first n_cu_limit mask
+ * bits leave out: other work, such as the GEMM of the other token split, can
+ * run there beside CU-limited fused calls without sharing CUs with them (the
+ * two-split overlap of [TWS]).  Same ownership and limits as
+ * tw_cu_masked_stream; it counts toward the 3 distinct masks of a process.
+ */
+tw_status tw_cu_complement_stream(int n_cu_limit, void** stream);
 
 /*
  * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts

@@ -44,7 +44,7 @@ _STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
 
 EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_fused_reduce_rmsnorm_allgather", "tw_reduce",
             "tw_rmsnorm", "tw_stream_copy",
-            "tw_cu_masked_stream",
+            "tw_cu_masked_stream", "tw_cu_complement_stream",
             "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
             "tw_last_error", "tw_abi_version")
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_stream_copy.restype = _c.c_int
     lib.tw_cu_masked_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
     lib.tw_cu_masked_stream.restype = _c.c_int
+    lib.tw_cu_complement_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
+    lib.tw_cu_complement_stream.restype = _c.c_int
     lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int, _c.c_int]
     lib.tw_set_fused_shape.restype = _c.c_int
     lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.c_int, _c.POINTER(_c.c_int),
@@ -282,6 +284,16 @@ def cu_masked_stream(n_cu_limit: int):
     torch = _torch()
     h = _vp()
     _check(load().tw_cu_masked_stream(int(n_cu_limit), ctypes.byref(h)))
+    return torch.cuda.ExternalStream(h.value)
+
+
+def cu_complement_stream(n_cu_limit: int):
+    """The library's stream on the CUs that `cu_masked_stream(n_cu_limit)`
+    leaves free (for other work beside CU-limited fused calls), as a torch
+    ExternalStream."""
+    torch = _torch()
+    h = _vp()
+    _check(load().tw_cu_complement_stream(int(n_cu_limit), ctypes.byref(h)))
     return torch.cuda.ExternalStream(h.value)
 
 

@@ -91,23 +91,27 @@ tw_status current_device_cus(int* cus_out) {
 // destroying queues on every call is avoided on purpose.  Caller holds g_mu.
 constexpr size_t kMaxMaskedStreams = 3;
 
-tw_status masked_stream(DeviceState& d, int k, hipStream_t* out) {
-  auto it = d.masked.find(k);
+// `key` > 0: the CUs of the first `key` mask bits; `key` < 0: the CUs the
+// first -key bits leave out (the complement, for work beside a CU-limited
+// call).
+tw_status masked_stream(DeviceState& d, int key, hipStream_t* out) {
+  auto it = d.masked.find(key);
   if (it != d.masked.end()) {
     *out = it->second;
     return TW_OK;
   }
   if (d.masked.size() >= kMaxMaskedStreams)
     return twv::fail(TW_ERR_UNSUPPORTED,
-                     "n_cu_limit %d: this process already uses %zu distinct CU limits (the "
+                     "CU mask %s%d: this process already uses %zu distinct CU masks (the "
                      "maximum; each needs its own hardware queue)",
-                     k, d.masked.size());
+                     key < 0 ? "complement of " : "", key < 0 ? -key : key, d.masked.size());
   std::vector<uint32_t> mask((d.cus + 31) / 32, 0u);
-  for (int i = 0; i < k; ++i) mask[i / 32] |= 1u << (i % 32);
+  const int lo = key > 0 ? 0 : -key, hi = key > 0 ? key : d.cus;
+  for (int i = lo; i < hi; ++i) mask[i / 32] |= 1u << (i % 32);
   hipStream_t s = nullptr;
   hipError_t e = hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data());
   if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask");
-  d.masked[k] = s;
+  d.masked[key] = s;
   *out = s;
   return TW_OK;
 }
@@ -251,7 +255,7 @@ tw_status tw_reduce(const void* const* partials, int n, int64_t rows, int64_t hi
              });
 }
 
-tw_status tw_cu_masked_stream(int n_cu_limit, void** stream) {
+static tw_status masked_stream_entry(int n_cu_limit, bool complement, void** stream) {
   twv::clear_error();
   if (stream == nullptr) return twv::fail(TW_ERR_INVALID_ARG, "stream is NULL");
   if (n_cu_limit < 1) return twv::fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 1");
@@ -263,10 +267,18 @@ tw_status tw_cu_masked_stream(int n_cu_limit, void** stream) {
     return twv::fail(TW_ERR_INVALID_ARG, "n_cu_limit %d is not below the device's %d CUs",
                      n_cu_limit, d->cus);
   hipStream_t ms = nullptr;
-  st = masked_stream(*d, n_cu_limit, &ms);
+  st = masked_stream(*d, complement ? -n_cu_limit : n_cu_limit, &ms);
   if (st != TW_OK) return st;
   *stream = static_cast<void*>(ms);
   return TW_OK;
+}
+
+tw_status tw_cu_masked_stream(int n_cu_limit, void** stream) {
+  return masked_stream_entry(n_cu_limit, false, stream);
+}
+
+tw_status tw_cu_complement_stream(int n_cu_limit, void** stream) {
+  return masked_stream_entry(n_cu_limit, true, stream);
 }
 
 tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit, void* stream) {

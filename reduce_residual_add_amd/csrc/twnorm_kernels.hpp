@@ -100,6 +100,7 @@ constexpr int kRsrcWord3 = 0x00020000;  // gfx9-family raw (untyped) buffer acce
 #ifndef TW_LOAD_CPOL
 #define TW_LOAD_CPOL 2    // NT
 #endif
+
 #ifndef TW_STORE_CPOL
 #define TW_STORE_CPOL 16  // SC1: device scope
 #endif
@@ -275,11 +276,13 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 #pragma unroll
   for (int k = 0; k < K; ++k) wv[k] = buf_load_cached(w_rsrc, lane_off + k * slot_stride);
 
+  // Row walk of this workgroup: first, first + stride, ... below `end`.
+  const int64_t first = blockIdx.x, stride = gridDim.x, end = rows;
   u32x4 raw[K][N + 1];
-  int64_t row = blockIdx.x;
-  if (row < rows) load_row<N, K>(raw, pp, residual, row * chunks, row_bytes, lane_off, slot_stride);
+  int64_t row = first;
+  if (row < end) load_row<N, K>(raw, pp, residual, row * chunks, row_bytes, lane_off, slot_stride);
   int parity = 0;
-  for (; row < rows; row += gridDim.x) {
+  for (; row < end; row += stride) {
     const int64_t base = row * chunks;
     const rsrc_t ro_rsrc = make_rsrc(residual_out + base, row_bytes);
     // Slots past the row's end loaded zeros, so they add nothing to ss, and
@@ -292,8 +295,8 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
       buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
     }
     // The raw registers are free again: start the next row's loads now.
-    const int64_t next = row + gridDim.x;
-    if (next < rows)
+    const int64_t next = row + stride;
+    if (next < end)
       load_row<N, K>(raw, pp, residual, next * chunks, row_bytes, lane_off, slot_stride);
 
     ss = team_sum(ss, 64);

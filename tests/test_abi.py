@@ -185,6 +185,8 @@ def test_masked_stream_argument_checks(lib):
     assert lib.tw_cu_masked_stream(8, None) == INV
     assert lib.tw_cu_masked_stream(0, ctypes.byref(h)) == INV
     assert lib.tw_cu_masked_stream(-3, ctypes.byref(h)) == INV
+    assert lib.tw_cu_complement_stream(8, None) == INV
+    assert lib.tw_cu_complement_stream(0, ctypes.byref(h)) == INV
 
 
 def test_error_is_cleared_by_next_call(lib):

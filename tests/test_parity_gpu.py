@@ -298,7 +298,7 @@ def test_fourth_cu_limit_is_refused(twn):
     for cu in (8, 16, 32):
         twn.fused_reduce_rmsnorm(parts, res, wt, 1e-5, n_cu_limit=cu)
     out = torch.zeros_like(res)
-    with pytest.raises(twn.TwError, match="distinct CU limits"):
+    with pytest.raises(twn.TwError, match="distinct CU masks"):
         twn.fused_reduce_rmsnorm(parts, res, wt, 1e-5, out=out, n_cu_limit=64)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(out)) == 0
@@ -390,3 +390,33 @@ def test_same_partial_twice(twn):
                                O.eps_as_passed(1e-5))
     assert_parity(from_dev(res_out, "bf16"), ref_res, "bf16", "residual_out")
     assert_parity(from_dev(out, "bf16"), ref_out, "bf16", "out")
+
+
+def test_results_unchanged_beside_a_gemm(twn):
+    """Fused calls on a CU-masked stream while a hipBLASLt GEMM runs on
+    another stream (the two-split overlap): the fused results are bit-identical
+    to a solo run, and the GEMM's too.  Uses the 32-CU mask the other tests
+    already hold (a process may hold three)."""
+    import torch
+    _say("[overlap] fused on 32 CUs beside a GEMM")
+    w = workloads.get("shard70b")
+    inp = workloads.make(w, seed=12, rows=512)
+    parts, res, wt = inputs_to_dev(inp)
+    a = torch.randn(1024, 3584, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(3584, 8192, device="cuda", dtype=torch.bfloat16)
+    solo_c = torch.matmul(a, b)
+    solo_out, solo_res = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    ms = twn.cu_masked_stream(32)
+    side = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(side):
+        cs = [torch.matmul(a, b) for _ in range(4)]
+    with torch.cuda.stream(ms):
+        for _ in range(4):
+            outs.append(twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], n_cu_limit=32))
+    torch.cuda.synchronize()
+    for o, r in outs:
+        assert torch.equal(o, solo_out) and torch.equal(r, solo_res)
+    for c in cs:
+        assert torch.equal(c, solo_c)
