@@ -49,15 +49,40 @@ EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_fused_reduce_rmsnorm_allgather", "tw_
             "tw_last_error", "tw_abi_version")
 
 
+def _hip_runtimes_loaded():
+    """Distinct HIP runtime files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libtwnorm.so (once).  Raises if it has not been built."""
+    """Load libtwnorm.so (once).  Raises if it has not been built.
+
+    torch is imported first so that the library binds to the HIP runtime
+    torch already uses: tensors, streams and kernels must all live in one
+    runtime.  Loading the library first would map a second HIP runtime into
+    the process, which then fails to find the device; that case is detected
+    and reported."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m reduce_residual_add_amd.build` (no CPU fallback exists)")
+    import torch  # noqa: F401  (binds the HIP runtime torch ships)
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process "
+                          f"({', '.join(sorted(runtimes))}); import torch before loading "
+                          "libtwnorm by any other route")
     lib.tw_fused_reduce_rmsnorm.argtypes = [_c.POINTER(_vp), _c.c_int, _i64, _i64, _c.c_int, _vp,
                                             _vp, _c.c_float, _vp, _vp, _c.c_int, _vp]
     lib.tw_fused_reduce_rmsnorm.restype = _c.c_int
