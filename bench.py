@@ -315,6 +315,12 @@ def measure_overlap(twn, w, sets, k, iters=40):
         fused_on_masked()
         gemm_on(comp)
 
+    side = torch.cuda.Stream()   # default priority, no CU mask
+
+    def both_unmasked_gemm():
+        fused_on_masked()
+        gemm_on(side)
+
     for f in (fused_on_masked, lambda: gemm_on(comp), lambda: gemm_on(torch.cuda.current_stream())):
         f()   # warm-up (hipBLASLt heuristics, code objects)
     res = {
@@ -323,6 +329,7 @@ def measure_overlap(twn, w, sets, k, iters=40):
         "gemm_on_complement_us": timed(lambda: gemm_on(comp)),
         "fused_on_k_cus_us": timed(fused_on_masked),
         "overlapped_us": timed(both),
+        "overlapped_gemm_unmasked_us": timed(both_unmasked_gemm),
     }
     gflop = 2.0 * w.rows * 3584 * w.hidden / 1e9
     res["gemm_tflops_all_cus"] = gflop / res["gemm_all_cus_us"] * 1e3   # GFLOP/us = PFLOP/s
