@@ -371,17 +371,24 @@ fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 // ---------------------------------------------------------------------------
 // Unfused comparison path, first kernel: reduced = round(sum_i p_i), a flat
 // grid-stride loop over 16-byte chunks (the reduce half of a ReduceScatter
-// written to HBM).
+// written to HBM).  It uses the same buffer addressing and cache policy as
+// the fused kernel, so the comparison measures the HBM round trip of the
+// intermediate and nothing else: each block-step gets descriptors based at
+// its first chunk and sized to the chunks left, and lanes past the end load
+// zeros and have their stores dropped.
 // ---------------------------------------------------------------------------
 template <class D, int N>
 __global__ void __launch_bounds__(256)
 reduce_kernel(PartialPtrs pp, u32x4* reduced, int64_t total_chunks) {
   constexpr int E = D::kElems;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total_chunks; c += stride) {
+  const unsigned lane_off = threadIdx.x * 16u;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b0 = (int64_t)blockIdx.x * blockDim.x; b0 < total_chunks; b0 += step) {
+    const int64_t left = total_chunks - b0;
+    const int bytes = int(left < int64_t(blockDim.x) ? left : int64_t(blockDim.x)) * 16;
     u32x4 raw[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) raw[i] = ld_stream(pp.p[i] + c);
+    for (int i = 0; i < N; ++i) raw[i] = buf_load(make_rsrc(pp.p[i] + b0, bytes), lane_off);
     float acc[E], t[E];
     widen(D{}, raw[0], acc);
 #pragma unroll
@@ -390,7 +397,7 @@ reduce_kernel(PartialPtrs pp, u32x4* reduced, int64_t total_chunks) {
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += t[e];
     }
-    st_stream(reduced + c, narrow(D{}, acc));
+    buf_store(narrow(D{}, acc), make_rsrc(reduced + b0, bytes), lane_off);
   }
 }
 
