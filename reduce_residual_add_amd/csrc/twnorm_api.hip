@@ -1,10 +1,11 @@
 // C-ABI entry points of libtwnorm (declared in include/twnorm.h).
 //
 // Each entry point validates its arguments without touching HIP
-// (twnorm_validate.cpp), picks the launch shape from (dtype, hidden) only, and
-// enqueues one kernel on the caller's stream -- or, for a CU limit, on a
+// (twnorm_validate.cpp), picks the launch shape from (dtype, hidden, n) only,
+// and enqueues one kernel on the caller's stream -- or, for a CU limit, on a
 // cached CU-masked stream that is ordered after the caller's stream and
-// before its later work by a pair of events.
+// before its later work by a pair of events (no join when the caller already
+// is that masked stream).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -21,7 +22,9 @@ namespace {
 
 struct DeviceState {
   int cus = 0;
-  std::map<int, hipStream_t> masked;  // n_cu_limit -> CU-masked stream
+  // CU-masked streams: key k > 0 = first k mask bits, k < 0 = complement of
+  // the first -k bits
+  std::map<int, hipStream_t> masked;
   hipEvent_t ev_in = nullptr;
   hipEvent_t ev_out = nullptr;
 };
@@ -83,17 +86,17 @@ tw_status current_device_cus(int* cus_out) {
   return TW_OK;
 }
 
-// A stream whose kernels may only occupy the CUs of the first `k` mask bits.
-// Streams keep the default priority.  Each CU-masked stream owns a hardware
-// queue of its own, and a process gets few of them (4 by default, shared
-// with the ordinary streams), so at most kMaxMaskedStreams distinct limits
-// are cached per device, for the life of the process; creating and
-// destroying queues on every call is avoided on purpose.  Caller holds g_mu.
+// CU-masked streams keep the default priority.  Each owns a hardware queue of
+// its own, and a process gets few of them (4 by default, shared with the
+// ordinary streams), so at most kMaxMaskedStreams distinct masks are cached
+// per device, for the life of the process; creating and destroying queues on
+// every call is avoided on purpose.
 constexpr size_t kMaxMaskedStreams = 3;
 
-// `key` > 0: the CUs of the first `key` mask bits; `key` < 0: the CUs the
-// first -key bits leave out (the complement, for work beside a CU-limited
-// call).
+// The stream for `key`: > 0, the CUs of the first `key` mask bits (the
+// hardware spreads consecutive bits round-robin over the 8 XCDs, then over
+// their shader engines); < 0, the CUs the first -key bits leave out (for work
+// beside a CU-limited call).  Caller holds g_mu.
 tw_status masked_stream(DeviceState& d, int key, hipStream_t* out) {
   auto it = d.masked.find(key);
   if (it != d.masked.end()) {
