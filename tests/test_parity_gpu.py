@@ -420,3 +420,46 @@ def test_results_unchanged_beside_a_gemm(twn):
         assert torch.equal(o, solo_out) and torch.equal(r, solo_res)
     for c in cs:
         assert torch.equal(c, solo_c)
+
+
+def test_graph_capture_replays(twn):
+    """The entry points allocate nothing and never synchronise, so a caller
+    can capture them in a HIP graph.  Three fused calls (and one unfused
+    pair) are captured, then replayed several times with eager work between
+    replays; every replay must reproduce the eager results bit for bit."""
+    import torch
+    _say("[graph] capture + replays")
+    w = workloads.get("shard70b")
+    inp = workloads.make(w, seed=21, rows=96)
+    parts, res, wt = inputs_to_dev(inp)
+    eager_out, eager_res = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    eager_red = twn.reduce(parts)
+    eager_out2, _ = twn.rmsnorm(eager_red, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(res) for _ in range(3)]
+    ress = [torch.empty_like(res) for _ in range(3)]
+    red = torch.empty_like(res)
+    out2 = torch.empty_like(res)
+    res2 = torch.empty_like(res)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the graph
+        twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=outs[0], residual_out=ress[0])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=outs[i], residual_out=ress[i])
+        twn.reduce(parts, out=red)
+        twn.rmsnorm(red, res, wt, inp["eps"], out=out2, residual_out=res2)
+    for rep in range(4):
+        for t in outs + ress + [red, out2, res2]:
+            t.fill_(-1.0)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert torch.equal(outs[i], eager_out), (rep, i)
+            assert torch.equal(ress[i], eager_res), (rep, i)
+        assert torch.equal(red, eager_red) and torch.equal(out2, eager_out2), rep
