@@ -254,6 +254,37 @@ def measure_unfused(twn, w, sets, steps, warmup):
     return time_steps([pair(d) for d in sets], steps, warmup)
 
 
+def measure_fused_graph(twn, w, sets, calls=64, replays=20):
+    """Per-call time of `calls` fused calls captured in one HIP graph and
+    replayed: the GPU-side cost without host launch overhead (which matters
+    for small, launch-bound calls)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in sets:
+            twn.fused_reduce_rmsnorm(d["parts"], d["res"], d["w"], w.eps, out=d["out"],
+                                     residual_out=d["res_out"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            d = sets[i % len(sets)]
+            twn.fused_reduce_rmsnorm(d["parts"], d["res"], d["w"], w.eps, out=d["out"],
+                                     residual_out=d["res_out"])
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / (replays * calls)
+
+
 def measure_allgather(twn, w, sets, steps, warmup):
     """The fused step with the AllGather store: each call writes its rows
     into N gather buffers of N * rows rows (one per simulated rank), at the
@@ -440,7 +471,9 @@ def main(argv=None):
             wd = w.with_rows(rows)
             dsets = make_sets(workloads.make(wd, seed=args.seed), 8)
             dms, _ = measure_fused(twn, wd, dsets, 0, 400, 40)
+            gms = measure_fused_graph(twn, wd, dsets)
             dec[str(rows)] = {"us_per_call": round(dms * 1e3, 3),
+                              "us_per_call_graph_replay": round(gms * 1e3, 3),
                               "gbs": round(wd.fused_bytes() / (dms * 1e-3) / 1e9, 1)}
             del dsets
         rep["decode_rows"] = dec
