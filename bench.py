@@ -82,6 +82,9 @@ def parse_args(argv=None):
     p.add_argument("--report", default="", help="write a detailed JSON report here")
     p.add_argument("--overlap-cus", type=int, default=32,
                    help="CUs given to the fused call in the --report two-split overlap")
+    p.add_argument("--unfused-steps", type=int, default=0,
+                   help="after the timed steps, run this many unfused reduce + norm pairs "
+                        "(for hardware-counter runs)")
     p.add_argument("--calibration-copies", type=int, default=0,
                    help="after the timed steps, run this many plain copies of "
                         f"{COPY_CAL_BYTES >> 20} MiB (hardware-counter calibration)")
@@ -434,6 +437,13 @@ def main(argv=None):
         # event join to the masked stream and back
         jms, _ = measure_fused(twn, w, sets, args.cu, max(20, args.steps // 5), 5)
         result["ms_per_step_joined_from_default_stream"] = round(jms, 6)
+
+    if args.unfused_steps > 0:
+        for i in range(args.unfused_steps):
+            d = sets[i % len(sets)]
+            twn.reduce(d["parts"], out=d["red"])
+            twn.rmsnorm(d["red"], d["res"], d["w"], w.eps, out=d["out"], residual_out=d["res_out"])
+        torch.cuda.synchronize()
 
     if args.calibration_copies > 0:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
