@@ -425,6 +425,9 @@ def main(argv=None):
         "config": {"workload": w.name, "n_partials": w.n, "rows": w.rows, "hidden": w.hidden,
                    "dtype": w.dtype, "eps": w.eps, "n_cu_limit": args.cu,
                    "rotating_sets": n_sets, "parallelism": "single GPU"},
+        "launch_shape": dict(zip(("waves_per_row", "chunks_per_lane", "team_lanes"),
+                                 twn.query_fused_shape(twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32,
+                                                       w.hidden, w.n))),
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "token_rows_per_s": round(rows_per_s, 1),
         "algorithmic_bytes_per_step": bytes_call,
