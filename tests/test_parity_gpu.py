@@ -463,3 +463,16 @@ def test_graph_capture_replays(twn):
             assert torch.equal(outs[i], eager_out), (rep, i)
             assert torch.equal(ress[i], eager_res), (rep, i)
         assert torch.equal(red, eager_red) and torch.equal(out2, eager_out2), rep
+
+
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_every_partial_count(twn, n):
+    """Each partial count is its own kernel instantiation: run every one of
+    them on the wide-row bf16 and fp32 kernels and on the narrow-row kernel."""
+    _say(f"[every n] n={n}")
+    for rows, hidden, dtype in [(7, 8192, "bf16"), (5, 1536, "f32"), (9, 128, "bf16"), (3, 40, "f32")]:
+        inp = workloads.make_random(n, rows, hidden, dtype, seed=100 * n + hidden)
+        out, res_out = _run_fused(twn, inp)
+        ref_out, ref_res = O.fused_from_storage(inp)
+        assert_parity(res_out, ref_res, dtype, f"n={n} H={hidden} {dtype} residual_out")
+        assert_parity(out, ref_out, dtype, f"n={n} H={hidden} {dtype} out")
