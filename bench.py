@@ -248,6 +248,31 @@ def measure_fused(twn, w, sets, cu, steps, warmup, stream=None):
     return ms, wall
 
 
+def measure_distribution(twn, w, sets, batches=60):
+    """Per-call times from `batches` batches of len(sets) back-to-back calls,
+    each batch between its own pair of events: median, p10 and p90 (us)."""
+    import torch
+    fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"])
+           for d in sets]
+    for f in fns * 3:
+        f()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(batches)]
+    for a, b in evs:
+        a.record()
+        for f in fns:
+            f()
+        b.record()
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) * 1e3 / len(fns) for a, b in evs)
+
+    def pct(q):
+        return per_call[min(len(per_call) - 1, int(q * len(per_call)))]
+    return {"batches": batches, "calls_per_batch": len(fns), "median_us": pct(0.5),
+            "p10_us": pct(0.1), "p90_us": pct(0.9)}
+
+
 def measure_unfused(twn, w, sets, steps, warmup):
     def pair(d):
         def f():
@@ -496,9 +521,11 @@ def main(argv=None):
         ov["sequential_all_cus_us"] = ov["gemm_all_cus_us"] + full_fused_us
         ov["overlap_speedup_vs_sequential"] = ov["sequential_all_cus_us"] / ov["overlapped_us"]
         rep["two_split_overlap"] = ov
+        rep["per_call_distribution"] = measure_distribution(twn, w, sets)
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
-        rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes,
-                               "gbs": 2 * cbytes / (cms * 1e-3) / 1e9}
+        copy_gbs = 2 * cbytes / (cms * 1e-3) / 1e9
+        rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes, "gbs": copy_gbs,
+                               "fused_frac_of_copy_ceiling": gbs / copy_gbs}
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
