@@ -408,8 +408,9 @@ def measure_copy(twn, total_bytes, steps, warmup):
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the multi-GPU "
-                                   "path is a design only (see DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library's path "
+                                   "covers one GPU's token shard and has no multi-GPU transport",
+                          "n_gpus": args.gpus}))
         return 2
     import torch
     import reduce_residual_add_amd as twn
