@@ -313,6 +313,34 @@ def measure_fused_graph(twn, w, sets, calls=64, replays=20):
     return start.elapsed_time(end) / (replays * calls)
 
 
+def measure_rows_scaling(twn, w, base_set, row_counts=(512, 1024, 2048, 4096, 8192)):
+    """Per-call time of the fused call at several row counts of the same
+    (dtype, H, N), each over rotating sets totalling at least twice the
+    Infinity Cache.  The larger inputs repeat the workload's rows on the
+    device: the values do not change the timing.  Returns {rows: {us, gbs}}."""
+    import torch
+    out = {}
+    per_row = (w.n + 3) * w.hidden * w.elem_bytes
+    for rows in row_counts:
+        reps = -(-rows // w.rows)
+        grow = lambda t: t.repeat(reps, 1)[:rows].contiguous()
+        n_sets = n_rotating_sets(rows * per_row, 0)
+        sets = []
+        for _ in range(n_sets):
+            res = grow(base_set["res"])
+            sets.append(dict(parts=[grow(p) for p in base_set["parts"]], res=res, w=base_set["w"],
+                             out=torch.empty_like(res), res_out=torch.empty_like(res)))
+        torch.cuda.synchronize()
+        steps = max(60, (300 * 1024) // rows)
+        ms = sorted(measure_fused(twn, w, sets, 0, steps, 20)[0] for _ in range(3))[1]
+        byt = rows * per_row + w.hidden * w.elem_bytes
+        out[str(rows)] = {"us_per_call": round(ms * 1e3, 2), "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                          "rotating_sets": n_sets}
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_allgather(twn, w, sets, steps, warmup):
     """The fused step with the AllGather store: each call writes its rows
     into N gather buffers of N * rows rows (one per simulated rank), at the
@@ -523,6 +551,8 @@ def main(argv=None):
         ov["overlap_speedup_vs_sequential"] = ov["sequential_all_cus_us"] / ov["overlapped_us"]
         rep["two_split_overlap"] = ov
         rep["per_call_distribution"] = measure_distribution(twn, w, sets)
+        if w.dtype == "bf16" and w.rows >= 64:
+            rep["rows_scaling"] = measure_rows_scaling(twn, w, sets[0])
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)
         copy_gbs = 2 * cbytes / (cms * 1e-3) / 1e9
         rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes, "gbs": copy_gbs,
