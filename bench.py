@@ -8,8 +8,11 @@ Default workload: N=8 partials of [1024, 8192] bf16 (one 8-way shard of
 rotating set of resident buffers; S sets totalling at least twice the 256 MB
 Infinity Cache are cycled so the timed bytes come from HBM, not the cache.
 
-Prints ONE JSON line.  --report PATH also writes a detailed JSON (other
-workloads, the unfused pair, the plain-copy ceiling, the CU-limit sweep).
+Prints ONE JSON line.  --report PATH also writes a detailed JSON: the
+unfused pair, the AllGather store, decode-size rows, the two-split overlap
+beside a GEMM, the per-call distribution, row-count scaling, the plain-copy
+ceiling, the ceiling of the fused call's own traffic pattern, and a
+cache-resident figure.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
 """
@@ -423,6 +426,20 @@ def measure_overlap(twn, w, sets, k, iters=40):
     return res
 
 
+def measure_mix(twn, w, sets, steps, warmup):
+    """The fused call's traffic pattern without its arithmetic
+    (tw_stream_mix): the N partials and the residual read, residual_out and
+    out written, on the same rotating buffers.  Returns (ms per call, bytes
+    moved per call)."""
+    fns = []
+    for d in sets:
+        srcs = list(d["parts"]) + [d["res"]]
+        dsts = [d["res_out"], d["out"]]
+        fns.append(lambda srcs=srcs, dsts=dsts: twn.stream_mix(srcs, dsts))
+    ms, _ = time_steps(fns, steps, warmup)
+    return ms, (w.n + 3) * w.rows * w.hidden * w.elem_bytes
+
+
 def measure_copy(twn, total_bytes, steps, warmup):
     import torch
     n = total_bytes // 2
@@ -557,6 +574,10 @@ def main(argv=None):
         copy_gbs = 2 * cbytes / (cms * 1e-3) / 1e9
         rep["copy_ceiling"] = {"ms": cms, "bytes_moved": 2 * cbytes, "gbs": copy_gbs,
                                "fused_frac_of_copy_ceiling": gbs / copy_gbs}
+        mms, mbytes = measure_mix(twn, w, sets, max(50, args.steps // 4), 10)
+        rep["mix_ceiling"] = {"ms": mms, "bytes_moved": mbytes,
+                              "gbs": mbytes / (mms * 1e-3) / 1e9,
+                              "fused_time_over_mix_time": ms / mms}
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}

@@ -164,6 +164,26 @@ tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_lim
                          void* stream);
 
 /*
+ * Measurement aid (not part of the method): the fused kernel's HBM traffic
+ * without its arithmetic, the practical ceiling of that traffic pattern.
+ * Reads n_src tensors of `bytes` bytes and writes n_dst tensors of the same
+ * size: every 32-bit word of every dst becomes the wrap-around uint32 sum of
+ * that word over the srcs.  The access pattern follows the fused kernel's
+ * row walk: 16 KiB blocks, each walked by one 256-lane workgroup (4 slots of
+ * 16 bytes per lane), the next block's loads issued before this block's
+ * stores, and a persistent grid of at most 2 workgroups per CU, with the
+ * fused kernel's cache policies (non-temporal loads, device-scope stores).
+ * So a fused call over N partials corresponds to n_src = N + 1, n_dst = 2
+ * and bytes = rows * hidden * element size.
+ * n_src in [1, TW_MAX_PARTIALS + 1], n_dst in [1, TW_MAX_PARTIALS]; bytes a
+ * multiple of 16; every pointer 16-byte aligned; no dst may overlap a src or
+ * another dst (srcs may overlap each other).  n_cu_limit as for the fused
+ * call.  bytes == 0 is a no-op.
+ */
+tw_status tw_stream_mix(const void* const* srcs, int n_src, void* const* dsts, int n_dst,
+                        int64_t bytes, int n_cu_limit, void* stream);
+
+/*
  * The library's CU-masked stream for `n_cu_limit` on the current device
  * (created on first use, owned by the library for the life of the process;
  * never destroy it).  Its kernels run only on the CUs of the first

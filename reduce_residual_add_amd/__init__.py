@@ -43,7 +43,7 @@ _STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
                  TW_ERR_HIP: "TW_ERR_HIP"}
 
 EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_fused_reduce_rmsnorm_allgather", "tw_reduce",
-            "tw_rmsnorm", "tw_stream_copy",
+            "tw_rmsnorm", "tw_stream_copy", "tw_stream_mix",
             "tw_cu_masked_stream", "tw_cu_complement_stream",
             "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
             "tw_last_error", "tw_abi_version")
@@ -97,6 +97,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_rmsnorm.restype = _c.c_int
     lib.tw_stream_copy.argtypes = [_vp, _vp, _i64, _c.c_int, _vp]
     lib.tw_stream_copy.restype = _c.c_int
+    lib.tw_stream_mix.argtypes = [_c.POINTER(_vp), _c.c_int, _c.POINTER(_vp), _c.c_int, _i64,
+                                  _c.c_int, _vp]
+    lib.tw_stream_mix.restype = _c.c_int
     lib.tw_cu_masked_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
     lib.tw_cu_masked_stream.restype = _c.c_int
     lib.tw_cu_complement_stream.argtypes = [_c.c_int, _c.POINTER(_vp)]
@@ -290,16 +293,46 @@ def rmsnorm(reduced, residual, weight, eps: float, *, out=None, residual_out=Non
     return out, residual_out
 
 
+def _check_raw(tensors, names, nbytes, device) -> None:
+    """GPU-resident, contiguous, on one device, each `nbytes` long."""
+    for t, name in zip(tensors, names):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() * t.element_size() != nbytes:
+            raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, expected {nbytes}")
+
+
 def stream_copy(src, dst, *, n_cu_limit: int = 0, stream=None):
     """dst = src byte for byte (measurement aid: the plain-copy ceiling)."""
     lib = load()
-    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
-        raise ValueError("src and dst sizes differ")
-    if not (src.is_contiguous() and dst.is_contiguous()):
-        raise ValueError("src and dst must be contiguous")
-    _check(lib.tw_stream_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
-                              int(n_cu_limit), _stream_ptr(stream)))
+    nbytes = src.numel() * src.element_size()
+    _check_raw((src, dst), ("src", "dst"), nbytes, src.device)
+    _check(lib.tw_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(n_cu_limit),
+                              _stream_ptr(stream)))
     return dst
+
+
+def stream_mix(srcs: Sequence, dsts: Sequence, *, n_cu_limit: int = 0, stream=None):
+    """Measurement aid: the fused kernel's traffic pattern without its
+    arithmetic.  Every 32-bit word of every dst becomes the wrap-around
+    uint32 sum of that word over the srcs (all of one byte size)."""
+    lib = load()
+    n_src, n_dst = len(srcs), len(dsts)
+    if n_src < 1 or n_src > TW_MAX_PARTIALS + 1 or n_dst < 1 or n_dst > TW_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TW_MAX_PARTIALS + 1} srcs and 1..{TW_MAX_PARTIALS} dsts")
+    nbytes = srcs[0].numel() * srcs[0].element_size()
+    _check_raw(list(srcs) + list(dsts), [f"srcs[{i}]" for i in range(n_src)] +
+               [f"dsts[{j}]" for j in range(n_dst)], nbytes, srcs[0].device)
+    if nbytes == 0:
+        return dsts
+    sa = (_vp * n_src)(*[t.data_ptr() for t in srcs])
+    da = (_vp * n_dst)(*[t.data_ptr() for t in dsts])
+    _check(lib.tw_stream_mix(sa, n_src, da, n_dst, nbytes, int(n_cu_limit), _stream_ptr(stream)))
+    return dsts
 
 
 def cu_masked_stream(n_cu_limit: int):

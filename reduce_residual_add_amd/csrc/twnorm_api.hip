@@ -296,4 +296,23 @@ tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_lim
              });
 }
 
+tw_status tw_stream_mix(const void* const* srcs, int n_src, void* const* dsts, int n_dst,
+                        int64_t bytes, int n_cu_limit, void* stream) {
+  twv::clear_error();
+  tw_status st = twv::check_mix(srcs, n_src, dsts, n_dst, bytes, n_cu_limit);
+  if (st != TW_OK) return st;
+  if (bytes == 0) return TW_OK;
+  int cus = 0;
+  st = current_device_cus(&cus);
+  if (st != TW_OK) return st;
+  twk::MixPtrs m{};
+  for (int i = 0; i < n_src; ++i) m.src[i] = static_cast<const twk::u32x4*>(srcs[i]);
+  for (int j = 0; j < n_dst; ++j) m.dst[j] = static_cast<twk::u32x4*>(dsts[j]);
+  m.n_dst = n_dst;
+  return run(n_cu_limit, static_cast<hipStream_t>(stream), "mix kernel launch",
+             [&](int cu, hipStream_t s) {
+               return twl::launch_mix(n_src, m, bytes, cu > 0 ? cu : cus, s);
+             });
+}
+
 }  // extern "C"

@@ -47,6 +47,13 @@ struct OutPtrs {
   int64_t row0;
 };
 
+// Sources and destinations of the traffic-pattern measurement aid.
+struct MixPtrs {
+  const u32x4* src[kMaxPartials + 1];
+  u32x4* dst[kMaxOutputs];
+  int n_dst;
+};
+
 // Storage formats.  A 16-byte chunk holds kElems values.
 struct Bf16 {
   static constexpr int kElems = 8;

@@ -47,5 +47,8 @@ hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* redu
                              int64_t total_chunks, int cu_limit, hipStream_t s);
 hipError_t launch_copy(const twk::u32x4* src, twk::u32x4* dst, int64_t chunks, int cu_limit,
                        hipStream_t s);
+// persistent_cus: CUs of the persistent grid (the CU limit, else the device's)
+hipError_t launch_mix(int n_src, const twk::MixPtrs& m, int64_t bytes, int persistent_cus,
+                      hipStream_t s);
 
 }  // namespace twl

@@ -211,6 +211,35 @@ tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_l
   return TW_OK;
 }
 
+tw_status check_mix(const void* const* srcs, int n_src, const void* const* dsts, int n_dst,
+                    int64_t bytes, int n_cu_limit) {
+  if (srcs == nullptr || dsts == nullptr) return fail(TW_ERR_INVALID_ARG, "srcs or dsts is NULL");
+  if (n_src < 1 || n_src > TW_MAX_PARTIALS + 1)
+    return fail(TW_ERR_INVALID_ARG, "n_src must be in [1, %d]", TW_MAX_PARTIALS + 1);
+  if (n_dst < 1 || n_dst > TW_MAX_PARTIALS)
+    return fail(TW_ERR_INVALID_ARG, "n_dst must be in [1, %d]", TW_MAX_PARTIALS);
+  if (bytes < 0) return fail(TW_ERR_INVALID_ARG, "bytes must be >= 0");
+  if (n_cu_limit < 0) return fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 0");
+  for (int i = 0; i < n_src; ++i)
+    if (srcs[i] == nullptr) return fail(TW_ERR_INVALID_ARG, "srcs[%d] is NULL", i);
+  for (int j = 0; j < n_dst; ++j)
+    if (dsts[j] == nullptr) return fail(TW_ERR_INVALID_ARG, "dsts[%d] is NULL", j);
+  if (bytes % 16 != 0) return fail(TW_ERR_UNSUPPORTED, "bytes must be a multiple of 16");
+  for (int i = 0; i < n_src; ++i)
+    if (misaligned(srcs[i])) return fail(TW_ERR_UNSUPPORTED, "srcs[%d] is not 16-byte aligned", i);
+  for (int j = 0; j < n_dst; ++j) {
+    if (misaligned(dsts[j])) return fail(TW_ERR_UNSUPPORTED, "dsts[%d] is not 16-byte aligned", j);
+    const Span d = span(dsts[j], bytes);
+    for (int i = 0; i < n_src; ++i)
+      if (overlap(d, span(srcs[i], bytes)))
+        return fail(TW_ERR_ALIAS, "dsts[%d] overlaps srcs[%d]", j, i);
+    for (int k = 0; k < j; ++k)
+      if (overlap(d, span(dsts[k], bytes)))
+        return fail(TW_ERR_ALIAS, "dsts[%d] overlaps dsts[%d]", j, k);
+  }
+  return TW_OK;
+}
+
 // Register-fit table of the wide-row kernels, generated at build time from the
 // compiler's resource remarks (reduce_residual_add_amd/build.py): which chunk
 // counts K run without scratch for each (dtype, n, launch bound).

@@ -36,6 +36,8 @@ tw_status check_fused_allgather(const void* const* partials, int n, int64_t rows
 tw_status check_reduce(const void* const* partials, int n, int64_t rows, int64_t hidden,
                        tw_dtype dtype, const void* reduced, int n_cu_limit);
 tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_limit);
+tw_status check_mix(const void* const* srcs, int n_src, const void* const* dsts, int n_dst,
+                    int64_t bytes, int n_cu_limit);
 
 // Shape for (dtype, hidden, n); honours the tw_set_fused_shape override.
 tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape);

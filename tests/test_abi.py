@@ -151,6 +151,42 @@ def test_reduce_rmsnorm_copy_validation(lib):
     assert lib.tw_stream_copy(b.parts[0], b.parts[1], 0, 0, None) == OK
 
 
+def test_stream_mix_validation(lib):
+    """Every check of tw_stream_mix fails before any HIP call.  The addresses
+    are fake: a call expected to succeed passes bytes == 0 (a no-op), so no
+    kernel is ever launched on them."""
+    b = Bufs()
+    base = 0x7F0000000000 + 4096 * MB
+    srcs = [base + i * 64 * MB for i in range(17)]
+    dsts = [base + (32 + j) * 64 * MB for j in range(16)]
+
+    def call(s=srcs[:9], d=dsts[:2], n_src=None, n_dst=None, nbytes=0, cu=0):
+        sa = None if s is None else (ctypes.c_void_p * max(1, len(s)))(*s)
+        da = None if d is None else (ctypes.c_void_p * max(1, len(d)))(*d)
+        n_src = len(s) if n_src is None else n_src
+        n_dst = len(d) if n_dst is None else n_dst
+        return lib.tw_stream_mix(sa, n_src, da, n_dst, nbytes, cu, None)
+    assert call() == OK
+    assert call(s=srcs, d=dsts) == OK                    # 17 sources, 16 destinations
+    assert call(s=None, n_src=1) == INV
+    assert call(d=None, n_dst=1) == INV
+    assert call(n_src=0) == INV
+    assert call(s=srcs + [srcs[0]]) == INV              # 18 sources
+    assert call(n_dst=0) == INV
+    assert call(d=dsts + [dsts[0]]) == INV              # 17 destinations
+    assert call(nbytes=-16) == INV
+    assert call(cu=-1) == INV
+    assert call(s=[srcs[0], None]) == INV
+    assert call(d=[dsts[0], None]) == INV
+    assert call(nbytes=1000) == UNS
+    assert call(s=[srcs[0] + 4]) == UNS
+    assert call(d=[dsts[0] + 8]) == UNS
+    assert call(s=[srcs[0], srcs[0]]) == OK                     # sources may coincide
+    assert call(d=[srcs[1] + 1024], nbytes=4096) == ALIAS       # dst inside a src
+    assert call(d=[dsts[0], dsts[0] + 2048], nbytes=4096) == ALIAS
+    del b
+
+
 def test_allgather_validation(lib):
     b = Bufs()
     tensor = b.rows * b.hidden * 2

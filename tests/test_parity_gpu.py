@@ -476,3 +476,42 @@ def test_every_partial_count(twn, n):
         ref_out, ref_res = O.fused_from_storage(inp)
         assert_parity(res_out, ref_res, dtype, f"n={n} H={hidden} {dtype} residual_out")
         assert_parity(out, ref_out, dtype, f"n={n} H={hidden} {dtype} out")
+
+
+# ---------------------------------------------------------------------------
+# Traffic-pattern measurement aid (not part of the method): every destination
+# word is the wrap-around uint32 sum of the source words; bytes past the end
+# stay untouched.  Checked against numpy integer arithmetic.
+# ---------------------------------------------------------------------------
+MIX_CASES = [
+    # (n_src, n_dst, bytes, n_cu_limit)
+    (1, 1, 4096, 0),                   # less than one block
+    (3, 2, 3 * 16384 + 48, 0),         # ragged last block, 4-slot layout
+    (9, 2, (16 << 20) + 16, 0),        # the shard70b pattern, one chunk past
+    (10, 3, 5 * 8192 + 4080, 0),       # 2-slot layout, ragged
+    (17, 2, 1 << 20, 0),               # the most sources
+    (9, 2, (2 << 20) + 512, 8),        # CU-limited persistent grid
+]
+
+
+@pytest.mark.parametrize("n_src,n_dst,nbytes,cu", MIX_CASES,
+                         ids=[f"s{a}-d{b}-{c}B-cu{d}" for a, b, c, d in MIX_CASES])
+def test_stream_mix_sums_words(twn, n_src, n_dst, nbytes, cu):
+    import torch
+    _say(f"[stream mix] n_src={n_src} n_dst={n_dst} bytes={nbytes} n_cu_limit={cu}")
+    words = nbytes // 4
+    rng = np.random.default_rng(1000 * n_src + n_dst)
+    host = [rng.integers(0, 2 ** 32, size=words, dtype=np.uint32) for _ in range(n_src)]
+    want = np.zeros(words, dtype=np.uint32)
+    for h in host:
+        want += h                       # wraps modulo 2**32
+    srcs = [torch.from_numpy(h.view(np.int32)).cuda() for h in host]
+    guard = 64
+    full = [torch.full((words + guard,), 7, dtype=torch.int32, device="cuda") for _ in range(n_dst)]
+    dsts = [f[:words] for f in full]
+    twn.stream_mix(srcs, dsts, n_cu_limit=cu)
+    torch.cuda.synchronize()
+    for j, f in enumerate(full):
+        got = f.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got[:words], want), f"dsts[{j}] differs"
+        assert (got[words:] == 7).all(), f"dsts[{j}] written past its end"

@@ -54,6 +54,20 @@ int main() {
   EXPECT(twv::check_fused_allgather(parts, 2, 4, 64, TW_BF16, res, w, 1e-5f, ag, 2, 4, 8, rout, 0), TW_OK);
   EXPECT(twv::check_fused_allgather(parts, 2, 4, 64, TW_BF16, res, w, 1e-5f, ag, 2, 5, 8, rout, 0), TW_ERR_INVALID_ARG);
   EXPECT(twv::check_fused_allgather(parts, 2, 4, 64, TW_BF16, res, w, 1e-5f, ag, 0, 0, 8, rout, 0), TW_ERR_INVALID_ARG);
+  // traffic-pattern measurement aid
+  const void* msrc[3] = {P(512), P(576), P(512)};   // sources may coincide
+  const void* mdst[2] = {P(640), P(704)};
+  EXPECT(twv::check_mix(msrc, 3, mdst, 2, 64 << 20, 0), TW_OK);
+  const void* madj[2] = {P(640), P(641)};            // adjacent 1 MiB ranges
+  EXPECT(twv::check_mix(msrc, 3, madj, 2, 1 << 20, 0), TW_OK);
+  EXPECT(twv::check_mix(msrc, 3, madj, 2, (1 << 20) + 16, 0), TW_ERR_ALIAS);
+  const void* mbad[1] = {P(520)};                    // inside srcs[0]'s 64 MiB
+  EXPECT(twv::check_mix(msrc, 3, mbad, 1, 64 << 20, 0), TW_ERR_ALIAS);
+  EXPECT(twv::check_mix(msrc, 0, mdst, 2, 1024, 0), TW_ERR_INVALID_ARG);
+  EXPECT(twv::check_mix(msrc, 18, mdst, 2, 1024, 0), TW_ERR_INVALID_ARG);
+  EXPECT(twv::check_mix(msrc, 3, mdst, 17, 1024, 0), TW_ERR_INVALID_ARG);
+  EXPECT(twv::check_mix(msrc, 3, mdst, 2, 1000, 0), TW_ERR_UNSUPPORTED);
+  EXPECT(twv::check_mix(nullptr, 3, mdst, 2, 1024, 0), TW_ERR_INVALID_ARG);
   // shape choice covers every width it accepts, for every n
   for (int n = 1; n <= 16; ++n)
     for (int64_t h = 8; h <= 65536; h += 8) {
