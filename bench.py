@@ -360,10 +360,19 @@ def measure_allgather(twn, w, sets, steps, warmup):
         fns.append(lambda d=d, off=off: twn.fused_reduce_rmsnorm_allgather(
             d["parts"], d["res"], d["w"], w.eps, gathers, off, residual_out=d["res_out"]))
     ms, _ = time_steps(fns, steps, warmup)
+    # the same traffic without the arithmetic: N partials and the residual
+    # read; residual_out and the N gather slices written
+    mix_fns = []
+    for i in range(len(sets) * ranks if ranks + 1 <= 16 else 0):
+        d = sets[i % len(sets)]
+        off = (i % ranks) * w.rows
+        dsts = [d["res_out"]] + [g[off:off + w.rows] for g in gathers]
+        mix_fns.append(lambda d=d, dsts=dsts: twn.stream_mix(list(d["parts"]) + [d["res"]], dsts))
+    mix_ms = time_steps(mix_fns, steps, warmup)[0] if mix_fns else float("nan")
     b = w.elem_bytes
     nbytes = (w.n + 2 + ranks) * w.rows * w.hidden * b + w.hidden * b
     del gathers
-    return ms, nbytes
+    return ms, nbytes, mix_ms
 
 
 def measure_overlap(twn, w, sets, k, iters=40):
@@ -545,9 +554,11 @@ def main(argv=None):
         rep["unfused_pair"] = {"ms_per_step": ums, "algorithmic_bytes": w.unfused_bytes(),
                                "gbs_on_unfused_bytes": w.unfused_bytes() / (ums * 1e-3) / 1e9,
                                "speedup_fused_vs_unfused": ums / ms}
-        ams, abytes = measure_allgather(twn, w, sets, max(50, args.steps // 4), 10)
+        ams, abytes, amix = measure_allgather(twn, w, sets, max(50, args.steps // 4), 10)
         rep["allgather_store"] = {"ms_per_step": ams, "algorithmic_bytes": abytes,
-                                  "gather_buffers": w.n, "gbs": abytes / (ams * 1e-3) / 1e9}
+                                  "gather_buffers": w.n, "gbs": abytes / (ams * 1e-3) / 1e9,
+                                  "traffic_pattern_ms": amix,
+                                  "fused_time_over_pattern_time": ams / amix}
         # decode-size rows: latency per call at a few row counts (same shape
         # as the full workload: the launch shape depends on (dtype, H, N) only)
         dec = {}
