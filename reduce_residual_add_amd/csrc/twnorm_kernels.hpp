@@ -269,12 +269,13 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
                   const u32x4* __restrict__ weight, OutPtrs outs, u32x4* residual_out,
                   int64_t rows, int chunks, float hidden_f, float eps) {
   constexpr int E = D::kElems;
-  __shared__ float red[2][MAXW];
+  __shared__ float red[2][MAXW * K];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int wave = tid >> 6;
   const int nwaves = nthr >> 6;
   const int row_bytes = chunks * 16;
+  const int groups = (chunks + 63) >> 6;  // 64-chunk groups of the row
   const unsigned lane_off = unsigned(tid) * 16u;      // this lane's first chunk
   const unsigned slot_stride = unsigned(nthr) * 16u;  // between a lane's chunk slots
 
@@ -295,10 +296,11 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
     // Slots past the row's end loaded zeros, so they add nothing to ss, and
     // their stores fall outside the descriptor's range and are dropped.
     float x[K][E];
-    float ss = 0.0f;
+    float q[K];  // sum of squares of each slot's chunk
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      add_chunk<D, N>(raw[k], x[k], ss);
+      q[k] = 0.0f;
+      add_chunk<D, N>(raw[k], x[k], q[k]);
       buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
     }
     // The raw registers are free again: start the next row's loads now.
@@ -306,16 +308,28 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
     if (next < end)
       load_row<N, K>(raw, pp, residual, next * chunks, row_bytes, lane_off, slot_stride);
 
-    ss = team_sum(ss, 64);
+    // Slot k of wave w holds chunks [64 g, 64 g + 64) with g = k W + w: one
+    // butterfly per slot gives each 64-chunk group's sum, and the groups are
+    // added in the order of g.  The order of every addition is thus fixed by
+    // the row width alone, whatever W and K are, and so are the bits.
+#pragma unroll
+    for (int k = 0; k < K; ++k) q[k] = team_sum(q[k], 64);
+    float ss = 0.0f;
     if (MAXW > 1 && nwaves > 1) {
-      if ((tid & 63) == 0) red[parity][wave] = ss;
+      if ((tid & 63) == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) red[parity][k * nwaves + wave] = q[k];
+      }
       __syncthreads();
-      ss = 0.0f;
-      for (int w = 0; w < nwaves; ++w) ss += red[parity][w];
-      // Double-buffered slot: the next row writes the other half, and the
-      // row after that is only reached once every wave passed the next
-      // barrier, i.e. finished reading this half.
+      for (int g = 0; g < groups; ++g) ss += red[parity][g];
+      // Double-buffered: the next row writes the other half, and the row
+      // after that is only reached once every wave passed the next barrier,
+      // i.e. finished reading this half.
       parity ^= 1;
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (k < groups) ss += q[k];
     }
     const float inv = 1.0f / __builtin_sqrtf(ss / hidden_f + eps);
     u32x4 o[K];

@@ -515,3 +515,50 @@ def test_stream_mix_sums_words(twn, n_src, n_dst, nbytes, cu):
         got = f.cpu().numpy().view(np.uint32)
         assert np.array_equal(got[:words], want), f"dsts[{j}] differs"
         assert (got[words:] == 7).all(), f"dsts[{j}] written past its end"
+
+
+# ---------------------------------------------------------------------------
+# The order of the sum of squares depends on the row width alone: every
+# launch shape (wavefronts x chunk slots, and the narrow-row kernel) gives
+# bit-identical results.  This is what lets the shape follow the row count
+# without breaking batch invariance.
+# ---------------------------------------------------------------------------
+INVARIANCE_CASES = [
+    # (n, rows, hidden, dtype)
+    (8, 6, 8192, "bf16"),     # 1024 chunks, 16 groups
+    (5, 4, 8200, "bf16"),     # 1025 chunks: a one-chunk last group
+    (4, 5, 5120, "bf16"),     # 640 chunks
+    (2, 7, 4096, "f32"),      # 1024 chunks of fp32
+    (3, 9, 200, "bf16"),      # 25 chunks: the narrow-row kernel by default
+    (2, 3, 1000, "f32"),      # 250 chunks, ragged last group
+]
+
+
+@pytest.mark.parametrize("n,rows,hidden,dtype", INVARIANCE_CASES,
+                         ids=[f"n{a}-r{b}-h{c}-{d}" for a, b, c, d in INVARIANCE_CASES])
+def test_results_independent_of_launch_shape(twn, n, rows, hidden, dtype):
+    import torch
+    inp = workloads.make_random(n, rows, hidden, dtype, seed=7 * hidden + n)
+    chunks = hidden * (2 if dtype == "bf16" else 4) // 16
+    auto = twn.query_fused_shape(0 if dtype == "bf16" else 1, hidden, n)
+    _say(f"[shape invariance] n={n} rows={rows} H={hidden} {dtype} auto={auto}")
+    ref_out, ref_res = _run_fused(twn, inp)
+    tried = 0
+    for waves in (1, 2, 3, 4, 5, 8, 16):
+        for k in (1, 2, 3, 4, 6, 8):
+            if waves * 64 * k < chunks or waves * 64 * k > 4 * max(chunks, 64) + 64 * 8:
+                continue
+            _say(f"  forced waves={waves} k={k}")
+            twn.set_fused_shape(waves, k)
+            try:
+                out, res_out = _run_fused(twn, inp)
+            finally:
+                twn.set_fused_shape(0, 0)
+            assert np.array_equal(res_out, ref_res), f"residual_out differs at {waves}x{k}"
+            assert np.array_equal(out.view(np.uint8), ref_out.view(np.uint8)), \
+                f"out differs at {waves}x{k} (auto {auto})"
+            tried += 1
+    assert tried >= 3
+    torch.cuda.synchronize()
+    ref = O.fused_from_storage(inp)
+    assert_parity(ref_out, ref[0], dtype, "out")
