@@ -480,6 +480,8 @@ def main(argv=None):
     n_sets = n_rotating_sets(set_bytes, args.rotate)
     sets = make_sets(inp, n_sets)
 
+    dev_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    call_cus = args.cu if 0 < args.cu < dev_cus else dev_cus
     masked = twn.cu_masked_stream(args.cu) if args.cu > 0 else None
     ms, wall = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup, stream=masked)
     bytes_call = w.fused_bytes()
@@ -507,7 +509,7 @@ def main(argv=None):
                    "rotating_sets": n_sets, "parallelism": "single GPU"},
         "launch_shape": dict(zip(("waves_per_row", "chunks_per_lane", "team_lanes"),
                                  twn.query_fused_shape(twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32,
-                                                       w.hidden, w.n))),
+                                                       w.hidden, w.n, w.rows, call_cus))),
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "token_rows_per_s": round(rows_per_s, 1),
         "algorithmic_bytes_per_step": bytes_call,
@@ -567,7 +569,10 @@ def main(argv=None):
             dsets = make_sets(workloads.make(wd, seed=args.seed), 8)
             dms, _ = measure_fused(twn, wd, dsets, 0, 400, 40)
             gms = measure_fused_graph(twn, wd, dsets)
-            dec[str(rows)] = {"us_per_call": round(dms * 1e3, 3),
+            dec[str(rows)] = {"launch_shape": list(twn.query_fused_shape(
+                                  twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32, w.hidden, w.n,
+                                  rows, call_cus)),
+                              "us_per_call": round(dms * 1e3, 3),
                               "us_per_call_graph_replay": round(gms * 1e3, 3),
                               "gbs": round(wd.fused_bytes() / (dms * 1e-3) / 1e9, 1)}
             del dsets

@@ -58,9 +58,12 @@
  *              life of the process: at most 3 distinct masks (limits k, and
  *              complements from tw_cu_complement_stream) per device and
  *              process; a fourth returns TW_ERR_UNSUPPORTED.
- *   Determinism The summation order depends only on (dtype, hidden, n): the
- *              same row gives the same bits whatever rows, shard offset or
- *              n_cu_limit are.
+ *   Determinism The order of every addition depends only on (dtype, hidden,
+ *              n): partials in index order per element, squares summed per
+ *              16-byte chunk, then per group of 64 consecutive chunks by a
+ *              fixed pairwise tree, then group by group in row order.  The
+ *              same row gives the same bits whatever rows, shard offset,
+ *              n_cu_limit or launch shape are.
  *   Threads    Entry points may be called from several host threads; the
  *              per-device cache (CU count, masked streams) is mutex-guarded.
  */
@@ -83,7 +86,7 @@ typedef enum {
 
 typedef enum { TW_BF16 = 0, TW_F32 = 1 } tw_dtype;
 
-#define TW_ABI_VERSION 1
+#define TW_ABI_VERSION 2
 #define TW_MAX_PARTIALS 16
 /* Largest supported row: 16 waves x 64 lanes x 8 chunks of 16 bytes. */
 #define TW_MAX_HIDDEN_BYTES (16 * 64 * 8 * 16)
@@ -211,18 +214,21 @@ tw_status tw_cu_complement_stream(int n_cu_limit, void** stream);
  * automatic choice), and cap the persistent grid at `wgs_per_cu` workgroups
  * per CU (0 = as many as the CU holds).  Applies to every later call on every
  * thread; a shape that cannot cover a row returns TW_ERR_UNSUPPORTED at the
- * call.  Changing the shape may change the last bit of results (a different
- * reduction tree); the grid cap never does.  Returns TW_ERR_INVALID_ARG for
+ * call.  Neither the shape nor the grid cap changes any result bit: every
+ * shape adds in the same order.  Returns TW_ERR_INVALID_ARG for
  * waves outside [0,16], chunks_per_lane not in {0,1,2,3,4,6,8}, only one of
  * the two being 0, or wgs_per_cu < 0.
  */
 tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu);
 
-/* Launch shape the fused kernel would use for (dtype, hidden, n partials);
- * writes the wavefronts per row and chunks per lane (team_lanes for rows
- * narrower than one wavefront, else 0).  HIP-free. */
-tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves,
-                               int* chunks_per_lane, int* team_lanes);
+/* Launch shape the fused kernel would use for (dtype, hidden, n partials)
+ * when `rows` rows run on `cus` CUs (the CU limit of the call, else the
+ * device's CU count); writes the wavefronts per row and chunks per lane
+ * (team_lanes for rows narrower than one wavefront, else 0).  Calls of fewer
+ * rows than CUs get as many wavefronts per row as the row fills; the results
+ * are the same bits for every shape.  HIP-free. */
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus,
+                               int* waves, int* chunks_per_lane, int* team_lanes);
 
 const char* tw_status_string(tw_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */

@@ -161,11 +161,12 @@ tw_status fused_launch(const void* const* partials, int n, int64_t rows, int64_t
                        const twk::OutPtrs& outs, void* residual_out, int n_cu_limit,
                        void* stream) {
   if (rows == 0) return TW_OK;
-  twv::Shape sh{};
-  tw_status st = twv::choose_shape(dtype, hidden, n, &sh);
-  if (st != TW_OK) return st;
   int cus = 0;
-  st = current_device_cus(&cus);
+  tw_status st = current_device_cus(&cus);
+  if (st != TW_OK) return st;
+  const int call_cus = (n_cu_limit > 0 && n_cu_limit < cus) ? n_cu_limit : cus;
+  twv::Shape sh{};
+  st = twv::choose_shape(dtype, hidden, n, rows, call_cus, &sh);
   if (st != TW_OK) return st;
 
   twl::FusedArgs a{};

@@ -1,6 +1,7 @@
 // Host-side argument validation and launch-shape choice (no HIP calls).
 #include "twnorm_validate.hpp"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -276,15 +277,20 @@ static const TunedShape kTuned[] = {
     {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
 };
 
-// Automatic shape:
+// Automatic shape.  The results do not depend on it (the order of every
+// addition is fixed by the row width), so it may follow the row count:
 //  * rows of at most 32 chunks: narrow-row kernel, smallest power-of-two team;
+//  * fewer rows than CUs (decode-sized calls, one workgroup per row, most CUs
+//    idle): as many wavefronts as the row fills (at most 16) with the fewest
+//    chunk slots per lane, so each lane issues the fewest loads in a row, if
+//    that spills nothing;
 //  * a measured shape for this (width, n) if it spills nothing;
 //  * else 4 wavefronts with the fewest chunk slots per lane that cover the
 //    row, if that spills nothing;
 //  * else, for each K the fewest wavefronts W <= 16 that cover the row, and
 //    among the spill-free (W, K) the fewest idle chunk slots (ties: smaller
 //    K); if every candidate spills, the fewest idle slots regardless.
-tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, Shape* shape) {
   const int b = elem_bytes(dtype);
   if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
   if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
@@ -302,6 +308,18 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, Shape* shape) {
     while (team < chunks) team <<= 1;
     *shape = Shape{0, 0, team};
     return TW_OK;
+  }
+  if (rows < cus) {
+    const int64_t w = std::min<int64_t>(16, (chunks + 63) / 64);
+    for (int k : kAllowedK) {
+      if (w * 64 * k >= chunks) {
+        if (!shape_spills(dtype, n, (int)w, k)) {
+          *shape = Shape{(int)w, k, 0};
+          return TW_OK;
+        }
+        break;
+      }
+    }
   }
   for (const TunedShape& t : kTuned) {
     if (t.elem_bytes == b && t.chunks == chunks && n >= t.n_lo && n <= t.n_hi &&
@@ -382,8 +400,8 @@ tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu) {
   return twv::set_override(waves, chunks_per_lane, wgs_per_cu);
 }
 
-tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves,
-                               int* chunks_per_lane, int* team_lanes) {
+tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus,
+                               int* waves, int* chunks_per_lane, int* team_lanes) {
   twv::clear_error();
   if (waves == nullptr || chunks_per_lane == nullptr || team_lanes == nullptr)
     return twv::fail(TW_ERR_INVALID_ARG, "output pointer is NULL");
@@ -392,8 +410,10 @@ tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int* waves
   if (hidden < 1) return twv::fail(TW_ERR_INVALID_ARG, "hidden must be >= 1");
   if ((hidden * b) % 16 != 0) return twv::fail(TW_ERR_UNSUPPORTED, "row bytes not a multiple of 16");
   if (hidden * b > TW_MAX_HIDDEN_BYTES) return twv::fail(TW_ERR_UNSUPPORTED, "row too wide");
+  if (rows < 0) return twv::fail(TW_ERR_INVALID_ARG, "rows must be >= 0");
+  if (cus < 1) return twv::fail(TW_ERR_INVALID_ARG, "cus must be >= 1");
   twv::Shape s{};
-  tw_status st = twv::choose_shape(dtype, hidden, n, &s);
+  tw_status st = twv::choose_shape(dtype, hidden, n, rows, cus, &s);
   if (st != TW_OK) return st;
   *waves = s.waves;
   *chunks_per_lane = s.k;

@@ -248,6 +248,19 @@ def test_shape_choice(lib):
     assert t == 0 and w * 64 * k >= 640
     w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8, 2)   # the widest row
     assert (w, k) == (16, 8)
+    # fewer rows than CUs: as many wavefronts as the row fills, fewest slots
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=1, cus=256) == (16, 1, 0)
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=255, cus=256) == (16, 1, 0)
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=256, cus=256) == (4, 4, 0)
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=64, cus=8) == (4, 4, 0)   # CU-limited
+    assert twn.query_fused_shape(BF16, 5120, 4, rows=8, cus=256) == (10, 1, 0)
+    assert twn.query_fused_shape(BF16, 4096, 2, rows=8, cus=256) == (8, 1, 0)
+    assert twn.query_fused_shape(BF16, 16384, 2, rows=8, cus=256) == (16, 2, 0)
+    assert twn.query_fused_shape(F32, 64, 2, rows=1, cus=256) == (0, 0, 16)   # still a team
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(BF16, 8192, 8, rows=-1)
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(BF16, 8192, 8, rows=4, cus=0)
     with pytest.raises(twn.TwError):
         twn.query_fused_shape(BF16, 12, 2)
     with pytest.raises(twn.TwError):
