@@ -562,3 +562,39 @@ def test_results_independent_of_launch_shape(twn, n, rows, hidden, dtype):
     torch.cuda.synchronize()
     ref = O.fused_from_storage(inp)
     assert_parity(ref_out, ref[0], dtype, "out")
+
+
+# ---------------------------------------------------------------------------
+# Tensors past 4 GiB: row offsets beyond 32 bits.  A seeded 1024-row block is
+# tiled on the device (data movement only), so row r holds host row r % 1024
+# and the oracle checks rows on both sides of the 4 GiB boundary.
+# ---------------------------------------------------------------------------
+def test_fused_tensors_beyond_4gib(twn):
+    import torch
+    n, hidden, block = 2, 8192, 1024
+    rows = 266240                      # 266240 x 16 KiB = 4.06 GiB per tensor
+    need = (n + 3) * rows * hidden * 2
+    free, _ = torch.cuda.mem_get_info()
+    if free < need + (4 << 30):
+        pytest.skip(f"needs {need / 2**30:.1f} GiB of free device memory")
+    _say(f"[beyond 4 GiB] n={n} rows={rows} H={hidden} bf16 ({need / 2**30:.1f} GiB)")
+    inp = workloads.make_random(n, block, hidden, "bf16", seed=44)
+    reps = rows // block
+    parts = [to_dev(p, "bf16").repeat(reps, 1) for p in inp["partials"]]
+    res = to_dev(inp["residual"], "bf16").repeat(reps, 1)
+    wt = to_dev(inp["weight"], "bf16")
+    out = torch.empty_like(res)
+    res_out = torch.empty_like(res)
+    twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=out, residual_out=res_out)
+    torch.cuda.synchronize()
+    boundary = (1 << 32) // (hidden * 2)       # first row whose offset needs bit 32
+    check = [0, 1, block - 1, boundary - 1, boundary, boundary + 1, boundary + 517, rows - 1]
+    idx = torch.tensor(check, device="cuda")
+    got_out = from_dev(out.index_select(0, idx), "bf16")
+    got_res = from_dev(res_out.index_select(0, idx), "bf16")
+    host_idx = np.array([r % block for r in check])
+    ref_out, ref_res = _oracle_rows(inp, host_idx)
+    assert_parity(got_res, ref_res, "bf16", "residual_out beyond 4 GiB")
+    assert_parity(got_out, ref_out, "bf16", "out beyond 4 GiB")
+    del parts, res, out, res_out
+    torch.cuda.empty_cache()
