@@ -313,3 +313,33 @@ def test_auto_shapes_never_spill(lib):
                         (mask[dt][n][_bucket(-(-chunks // (64 * kk)))] >> K_VALUES.index(kk)) & 1]
                 if free:
                     assert (mask[dt][n][_bucket(w)] >> K_VALUES.index(k)) & 1, (dt, n, hidden, w, k)
+
+
+def test_last_error_is_per_thread(lib):
+    """Each thread sees the detail of its own last failure (ctypes releases
+    the GIL during the calls, so the threads run the library concurrently)."""
+    import threading
+    b = Bufs()
+    results = {}
+
+    def worker(tid):
+        msgs = set()
+        for i in range(400):
+            if tid % 2 == 0:
+                st = b.fused(lib, n=0)                     # n out of range
+                want = "n must be in [1, 16]"
+            else:
+                st = b.fused(lib, hidden=12)               # 24-byte rows
+                want = "multiple of 16"
+            msg = twn.last_error()
+            msgs.add((st, want in msg))
+        results[tid] = msgs
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for tid, msgs in results.items():
+        want_status = INV if tid % 2 == 0 else UNS
+        assert msgs == {(want_status, True)}, (tid, msgs)

@@ -598,3 +598,45 @@ def test_fused_tensors_beyond_4gib(twn):
     assert_parity(got_out, ref_out, "bf16", "out beyond 4 GiB")
     del parts, res, out, res_out
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Host threads: several threads issue fused calls concurrently, each on its
+# own stream; every result is bit-identical to the single-threaded one.
+# ---------------------------------------------------------------------------
+def test_concurrent_host_threads(twn):
+    import threading
+    import torch
+    _say("[threads] 4 host threads x 20 calls, own streams")
+    cases = [workloads.make_random(n, rows, h, "bf16", seed=90 + n)
+             for n, rows, h in ((2, 64, 4096), (4, 33, 5120), (8, 300, 8192), (3, 7, 200))]
+    dev = [inputs_to_dev(c) for c in cases]
+    ref = []
+    for c, (parts, res, wt) in zip(cases, dev):
+        o, r = twn.fused_reduce_rmsnorm(parts, res, wt, c["eps"])
+        torch.cuda.synchronize()
+        ref.append((from_dev(o, "bf16"), from_dev(r, "bf16")))
+    errors = []
+
+    def worker(i):
+        try:
+            c, (parts, res, wt) = cases[i], dev[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [twn.fused_reduce_rmsnorm(parts, res, wt, c["eps"]) for _ in range(20)]
+            s.synchronize()
+            for o, r in outs:
+                if not (np.array_equal(from_dev(o, "bf16"), ref[i][0])
+                        and np.array_equal(from_dev(r, "bf16"), ref[i][1])):
+                    errors.append(f"thread {i}: result differs")
+                    return
+        except Exception as e:  # reported below
+            errors.append(f"thread {i}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
