@@ -253,6 +253,9 @@ MUTANTS = {
     "weight_reversed": _fused_with(norm=lambda x, w, eps: O.rmsnorm(x, np.asarray(w)[::-1], eps)),
     "mean_over_tokens": _fused_with(norm=lambda x, w, eps: x / np.sqrt(np.mean(x * x, axis=0, keepdims=True) + eps) * w),
     "sqrt_not_inverse": _fused_with(norm=lambda x, w, eps: x * np.sqrt(np.mean(x * x, -1) + eps)[..., None] * w),
+    "sum_not_mean": _fused_with(norm=_norm_divisor(lambda h: 1)),
+    "eps_squared": _fused_with(norm=lambda x, w, eps: O.rmsnorm(x, w, eps * eps)),
+    "weight_shifted": _fused_with(norm=lambda x, w, eps: O.rmsnorm(x, np.roll(np.asarray(w), 1), eps)),
     "residual_out_is_norm": None,   # handled below
 }
 
