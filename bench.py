@@ -11,8 +11,8 @@ Infinity Cache are cycled so the timed bytes come from HBM, not the cache.
 Prints ONE JSON line.  --report PATH also writes a detailed JSON: the
 unfused pair, the AllGather store, decode-size rows, the two-split overlap
 beside a GEMM, the per-call distribution, row-count scaling, the plain-copy
-ceiling, the ceiling of the fused call's own traffic pattern, and a
-cache-resident figure.
+ceiling, the ceiling of the fused call's own traffic pattern, the same step
+as plain eager PyTorch ops, and a cache-resident figure.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
 """
@@ -449,6 +449,26 @@ def measure_mix(twn, w, sets, steps, warmup):
     return ms, (w.n + 3) * w.rows * w.hidden * w.elem_bytes
 
 
+def measure_torch_eager(w, sets, steps, warmup):
+    """The same step written as plain eager PyTorch ops (float32 arithmetic,
+    stores in the storage dtype), on the same rotating buffers: context for
+    what the fusion saves, not part of the library."""
+    import torch
+
+    def step(d):
+        x = d["parts"][0].float()
+        for p in d["parts"][1:]:
+            x += p.float()
+        x += d["res"].float()
+        d["res_out"].copy_(x)
+        inv = torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + w.eps)
+        d["out"].copy_(x * inv * d["w"].float())
+
+    fns = [lambda d=d: step(d) for d in sets]
+    ms, _ = time_steps(fns, steps, warmup)
+    return ms
+
+
 def measure_copy(twn, total_bytes, steps, warmup):
     import torch
     n = total_bytes // 2
@@ -594,6 +614,9 @@ def main(argv=None):
         rep["mix_ceiling"] = {"ms": mms, "bytes_moved": mbytes,
                               "gbs": mbytes / (mms * 1e-3) / 1e9,
                               "fused_time_over_mix_time": ms / mms}
+        tms = measure_torch_eager(w, sets, max(20, args.steps // 10), 5)
+        rep["torch_eager_same_step"] = {"ms": tms, "gbs_on_fused_bytes": bytes_call / (tms * 1e-3) / 1e9,
+                                        "fused_speedup": tms / ms}
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
