@@ -175,6 +175,23 @@ def _rows_hidden(t):
     return int(t.shape[0]), int(t.shape[1])
 
 
+def _check_fused_tensors(partials, residual, weight, out, residual_out):
+    """Device, dtype, shape and contiguity of a fused call's tensors; returns
+    (rows, hidden, n)."""
+    rows, hidden = _rows_hidden(residual)
+    dt, dev = residual.dtype, residual.device
+    n = len(partials)
+    if n < 1 or n > TW_MAX_PARTIALS:
+        raise ValueError(f"need 1..{TW_MAX_PARTIALS} partials, got {n}")
+    for i, p in enumerate(partials):
+        _check_tensor(p, f"partials[{i}]", (rows, hidden), dt, dev)
+    _check_tensor(residual, "residual", (rows, hidden), dt, dev)
+    _check_tensor(weight, "weight", (hidden,), dt, dev)
+    _check_tensor(out, "out", (rows, hidden), dt, dev)
+    _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    return rows, hidden, n
+
+
 # ---------------------------------------------------------------------------
 # Entry points
 # ---------------------------------------------------------------------------
@@ -187,21 +204,11 @@ def fused_reduce_rmsnorm(partials: Sequence, residual, weight, eps: float, *, ou
     residual update.  Returns (out, residual_out)."""
     torch = _torch()
     lib = load()
-    rows, hidden = _rows_hidden(residual)
-    dt, dev = residual.dtype, residual.device
-    n = len(partials)
-    if n < 1 or n > TW_MAX_PARTIALS:
-        raise ValueError(f"need 1..{TW_MAX_PARTIALS} partials, got {n}")
-    for i, p in enumerate(partials):
-        _check_tensor(p, f"partials[{i}]", (rows, hidden), dt, dev)
-    _check_tensor(residual, "residual", (rows, hidden), dt, dev)
-    _check_tensor(weight, "weight", (hidden,), dt, dev)
     if out is None:
         out = torch.empty_like(residual)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
-    _check_tensor(out, "out", (rows, hidden), dt, dev)
-    _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    rows, hidden, n = _check_fused_tensors(partials, residual, weight, out, residual_out)
     if rows == 0:   # nothing to do (an empty tensor's data_ptr() may be NULL)
         return out, residual_out
     arr = (_vp * n)(*[p.data_ptr() for p in partials])
@@ -379,15 +386,17 @@ class PreparedFused:
     def __init__(self, partials, residual, weight, eps, out, residual_out, n_cu_limit=0,
                  stream=None):
         self._lib = load()
+        rows, hidden, self._n = _check_fused_tensors(partials, residual, weight, out, residual_out)
+        self._rows = rows
         self._keep = (list(partials), residual, weight, out, residual_out)
-        self._n = len(partials)
         self._arr = (_vp * self._n)(*[p.data_ptr() for p in partials])
-        rows, hidden = _rows_hidden(residual)
         self._args = (self._arr, self._n, rows, hidden, dtype_code(residual), residual.data_ptr(),
                       weight.data_ptr(), ctypes.c_float(float(eps)), out.data_ptr(),
                       residual_out.data_ptr(), int(n_cu_limit), _stream_ptr(stream))
 
     def __call__(self) -> None:
+        if self._rows == 0:
+            return
         st = self._lib.tw_fused_reduce_rmsnorm(*self._args)
         if st != TW_OK:
             _check(st)

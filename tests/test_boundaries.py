@@ -92,3 +92,9 @@ def test_host_tensors_are_refused():
         twn.reduce(parts)
     with pytest.raises((ValueError, ImportError)):
         twn.rmsnorm(res, res, w, 1e-5)
+    with pytest.raises((ValueError, ImportError)):
+        twn.PreparedFused(parts, res, w, 1e-5, torch.empty_like(res), torch.empty_like(res))
+    with pytest.raises((ValueError, ImportError)):
+        twn.stream_copy(res, torch.empty_like(res))
+    with pytest.raises((ValueError, ImportError)):
+        twn.stream_mix([res], [torch.empty_like(res)])
