@@ -1,8 +1,8 @@
 // C-ABI entry points of libtwnorm (declared in include/twnorm.h).
 //
 // Each entry point validates its arguments without touching HIP
-// (twnorm_validate.cpp), picks the launch shape from (dtype, hidden, n) only,
-// and enqueues one kernel on the caller's stream -- or, for a CU limit, on a
+// (twnorm_validate.cpp), picks the launch shape from (dtype, hidden, n) and
+// the call's rows and CUs (every shape gives the same bits), and enqueues one kernel on the caller's stream -- or, for a CU limit, on a
 // cached CU-masked stream that is ordered after the caller's stream and
 // before its later work by a pair of events (no join when the caller already
 // is that masked stream).
