@@ -581,8 +581,8 @@ def main(argv=None):
                                   "gather_buffers": w.n, "gbs": abytes / (ams * 1e-3) / 1e9,
                                   "traffic_pattern_ms": amix,
                                   "fused_time_over_pattern_time": ams / amix}
-        # decode-size rows: latency per call at a few row counts (same shape
-        # as the full workload: the launch shape depends on (dtype, H, N) only)
+        # decode-size rows: latency per call at a few row counts of the same
+        # (dtype, H, N); below the CU count the kernel runs its latency shape
         dec = {}
         for rows in (1, 8, 64):
             wd = w.with_rows(rows)
