@@ -273,6 +273,7 @@ struct TunedShape {
 };
 static const TunedShape kTuned[] = {
     {2, 1024, 5, 16, 4, 4},  // 8192 bf16 features, many partials
+    {2, 1024, 1, 3, 8, 2},   // 8192 bf16 features, few partials
     {2, 512, 1, 3, 8, 1},    // 4096 bf16 features, few partials
     {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
 };
