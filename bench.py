@@ -529,7 +529,7 @@ def main(argv=None):
                    "rotating_sets": n_sets, "parallelism": "single GPU"},
         "launch_shape": dict(zip(("waves_per_row", "chunks_per_lane", "team_lanes"),
                                  twn.query_fused_shape(twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32,
-                                                       w.hidden, w.n, w.rows, call_cus))),
+                                                       w.hidden, w.n, w.rows, call_cus, dev_cus))),
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "token_rows_per_s": round(rows_per_s, 1),
         "algorithmic_bytes_per_step": bytes_call,
@@ -591,7 +591,7 @@ def main(argv=None):
             gms = measure_fused_graph(twn, wd, dsets)
             dec[str(rows)] = {"launch_shape": list(twn.query_fused_shape(
                                   twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32, w.hidden, w.n,
-                                  rows, call_cus)),
+                                  rows, call_cus, dev_cus)),
                               "us_per_call": round(dms * 1e3, 3),
                               "us_per_call_graph_replay": round(gms * 1e3, 3),
                               "gbs": round(wd.fused_bytes() / (dms * 1e-3) / 1e9, 1)}

@@ -86,7 +86,7 @@ typedef enum {
 
 typedef enum { TW_BF16 = 0, TW_F32 = 1 } tw_dtype;
 
-#define TW_ABI_VERSION 2
+#define TW_ABI_VERSION 3
 #define TW_MAX_PARTIALS 16
 /* Largest supported row: 16 waves x 64 lanes x 8 chunks of 16 bytes. */
 #define TW_MAX_HIDDEN_BYTES (16 * 64 * 8 * 16)
@@ -223,12 +223,16 @@ tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu);
 
 /* Launch shape the fused kernel would use for (dtype, hidden, n partials)
  * when `rows` rows run on `cus` CUs (the CU limit of the call, else the
- * device's CU count); writes the wavefronts per row and chunks per lane
- * (team_lanes for rows narrower than one wavefront, else 0).  Calls of fewer
- * rows than CUs get as many wavefronts per row as the row fills; the results
- * are the same bits for every shape.  HIP-free. */
+ * device's count) of a device with `device_cus` CUs; writes the wavefronts
+ * per row and chunks per lane (team_lanes for rows narrower than one
+ * wavefront, else 0).  Calls of fewer rows than CUs get as many wavefronts
+ * per row as the row fills; calls on at most half of the device's CUs may
+ * get a shape measured for that regime instead of the whole-chip one.
+ * The results are the same bits for every shape.  Needs
+ * 1 <= cus <= device_cus and rows >= 0.  HIP-free. */
 tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus,
-                               int* waves, int* chunks_per_lane, int* team_lanes);
+                               int device_cus, int* waves, int* chunks_per_lane,
+                               int* team_lanes);
 
 const char* tw_status_string(tw_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libtwnorm.so")
 TW_OK, TW_ERR_INVALID_ARG, TW_ERR_UNSUPPORTED, TW_ERR_ALIAS, TW_ERR_HIP = 0, -1, -2, -3, -4
 TW_BF16, TW_F32 = 0, 1
 TW_MAX_PARTIALS = 16
-TW_ABI_VERSION = 2
+TW_ABI_VERSION = 3
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -106,7 +106,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_cu_complement_stream.restype = _c.c_int
     lib.tw_set_fused_shape.argtypes = [_c.c_int, _c.c_int, _c.c_int]
     lib.tw_set_fused_shape.restype = _c.c_int
-    lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.c_int, _i64, _c.c_int,
+    lib.tw_query_fused_shape.argtypes = [_c.c_int, _i64, _c.c_int, _i64, _c.c_int, _c.c_int,
                                          _c.POINTER(_c.c_int),
                                          _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]
     lib.tw_query_fused_shape.restype = _c.c_int
@@ -369,13 +369,16 @@ def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0, wgs_per_cu: int = 
     _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane), int(wgs_per_cu)))
 
 
-def query_fused_shape(dtype: int, hidden: int, n: int, rows: int = 1 << 40, cus: int = 256):
+def query_fused_shape(dtype: int, hidden: int, n: int, rows: int = 1 << 40, cus: int = 256,
+                      device_cus: int = 256):
     """(waves, chunks_per_lane, team_lanes) the fused kernel uses for n
-    partials of rows `hidden` wide when `rows` rows run on `cus` CUs (the
-    defaults: a call large enough to fill the whole chip)."""
+    partials of rows `hidden` wide when `rows` rows run on `cus` of the
+    device's `device_cus` CUs (the defaults: a call large enough to fill a
+    whole 256-CU chip)."""
     w, k, t = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(load().tw_query_fused_shape(int(dtype), int(hidden), int(n), int(rows), int(cus),
-                                       ctypes.byref(w), ctypes.byref(k), ctypes.byref(t)))
+                                       int(device_cus), ctypes.byref(w), ctypes.byref(k),
+                                       ctypes.byref(t)))
     return w.value, k.value, t.value
 
 

@@ -166,7 +166,7 @@ tw_status fused_launch(const void* const* partials, int n, int64_t rows, int64_t
   if (st != TW_OK) return st;
   const int call_cus = (n_cu_limit > 0 && n_cu_limit < cus) ? n_cu_limit : cus;
   twv::Shape sh{};
-  st = twv::choose_shape(dtype, hidden, n, rows, call_cus, &sh);
+  st = twv::choose_shape(dtype, hidden, n, rows, call_cus, cus, &sh);
   if (st != TW_OK) return st;
 
   twl::FusedArgs a{};

@@ -278,50 +278,24 @@ static const TunedShape kTuned[] = {
     {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
 };
 
-// Automatic shape.  The results do not depend on it (the order of every
-// addition is fixed by the row width), so it may follow the row count:
-//  * rows of at most 32 chunks: narrow-row kernel, smallest power-of-two team;
-//  * fewer rows than CUs (decode-sized calls, one workgroup per row, most CUs
-//    idle): as many wavefronts as the row fills (at most 16) with the fewest
-//    chunk slots per lane, so each lane issues the fewest loads in a row, if
-//    that spills nothing;
+// Shapes measured fastest when a call runs on at most half of the CUs: on 8,
+// 16, 32 and 64 CUs, 8 x 2 beats the whole-chip 4 x 4 by 4-6% on 8192-wide
+// rows with 8 partials; on 32 CUs, 10 x 1 beats 8 x 2 by 15% on 5120-wide
+// rows with 4 partials (every lane busy, three rows in flight per CU).
+static const TunedShape kTunedLimited[] = {
+    {2, 1024, 5, 16, 8, 2},
+    {2, 640, 3, 6, 10, 1},
+};
+
+// The whole-chip shape of a wide row:
 //  * a measured shape for this (width, n) if it spills nothing;
 //  * else 4 wavefronts with the fewest chunk slots per lane that cover the
 //    row, if that spills nothing;
 //  * else, for each K the fewest wavefronts W <= 16 that cover the row, and
 //    among the spill-free (W, K) the fewest idle chunk slots (ties: smaller
 //    K); if every candidate spills, the fewest idle slots regardless.
-tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, Shape* shape) {
-  const int b = elem_bytes(dtype);
-  if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
-  if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
-  const int64_t chunks = hidden * b / 16;
-  const int ow = g_override_waves.load(), ok = g_override_k.load();
-  if (ow > 0 && ok > 0) {
-    if ((int64_t)ow * 64 * ok < chunks)
-      return fail(TW_ERR_UNSUPPORTED, "forced shape %d waves x %d chunks cannot cover %lld chunks",
-                  ow, ok, (long long)chunks);
-    *shape = Shape{ow, ok, 0};
-    return TW_OK;
-  }
-  if (chunks <= 32) {
-    int team = 1;
-    while (team < chunks) team <<= 1;
-    *shape = Shape{0, 0, team};
-    return TW_OK;
-  }
-  if (rows < cus) {
-    const int64_t w = std::min<int64_t>(16, (chunks + 63) / 64);
-    for (int k : kAllowedK) {
-      if (w * 64 * k >= chunks) {
-        if (!shape_spills(dtype, n, (int)w, k)) {
-          *shape = Shape{(int)w, k, 0};
-          return TW_OK;
-        }
-        break;
-      }
-    }
-  }
+static tw_status throughput_shape(tw_dtype dtype, int b, int64_t chunks, int64_t hidden, int n,
+                                  Shape* shape) {
   for (const TunedShape& t : kTuned) {
     if (t.elem_bytes == b && t.chunks == chunks && n >= t.n_lo && n <= t.n_hi &&
         !shape_spills(dtype, n, t.waves, t.k)) {
@@ -357,6 +331,65 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
   }
   if (any_waste < 0) return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide", (long long)hidden);
   *shape = best_waste >= 0 ? Shape{best_w, best_k, 0} : Shape{any_w, any_k, 0};
+  return TW_OK;
+}
+
+// Automatic shape.  The results do not depend on it (the order of every
+// addition is fixed by the row width), so it may follow the call:
+//  * rows of at most 32 chunks: narrow-row kernel, smallest power-of-two team;
+//  * fewer rows than CUs (decode-sized calls, one workgroup per row, most CUs
+//    idle): as many wavefronts as the row fills (at most 16) with the fewest
+//    chunk slots per lane, so each lane issues the fewest loads in a row, if
+//    that spills nothing;
+//  * else the whole-chip shape above, or, when the call runs on at most half
+//    of the device's CUs, a shape measured for that regime if there is one.
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, int device_cus,
+                       Shape* shape) {
+  const int b = elem_bytes(dtype);
+  if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
+  if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
+  const int64_t chunks = hidden * b / 16;
+  const int ow = g_override_waves.load(), ok = g_override_k.load();
+  if (ow > 0 && ok > 0) {
+    if ((int64_t)ow * 64 * ok < chunks)
+      return fail(TW_ERR_UNSUPPORTED, "forced shape %d waves x %d chunks cannot cover %lld chunks",
+                  ow, ok, (long long)chunks);
+    *shape = Shape{ow, ok, 0};
+    return TW_OK;
+  }
+  if (chunks <= 32) {
+    int team = 1;
+    while (team < chunks) team <<= 1;
+    *shape = Shape{0, 0, team};
+    return TW_OK;
+  }
+  if (rows < cus) {
+    const int64_t w = std::min<int64_t>(16, (chunks + 63) / 64);
+    for (int k : kAllowedK) {
+      if (w * 64 * k >= chunks) {
+        if (!shape_spills(dtype, n, (int)w, k)) {
+          *shape = Shape{(int)w, k, 0};
+          return TW_OK;
+        }
+        break;
+      }
+    }
+  }
+  Shape t{};
+  tw_status st = throughput_shape(dtype, b, chunks, hidden, n, &t);
+  if (st != TW_OK) return st;
+  // On at most half of the device's CUs a call is bound by what each CU
+  // issues and keeps in flight, not by HBM, and other shapes win there.
+  if (2 * (int64_t)cus <= device_cus) {
+    for (const TunedShape& u : kTunedLimited) {
+      if (u.elem_bytes == b && u.chunks == chunks && n >= u.n_lo && n <= u.n_hi &&
+          !shape_spills(dtype, n, u.waves, u.k)) {
+        t = Shape{u.waves, u.k, 0};
+        break;
+      }
+    }
+  }
+  *shape = t;
   return TW_OK;
 }
 
@@ -402,7 +435,8 @@ tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu) {
 }
 
 tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus,
-                               int* waves, int* chunks_per_lane, int* team_lanes) {
+                               int device_cus, int* waves, int* chunks_per_lane,
+                               int* team_lanes) {
   twv::clear_error();
   if (waves == nullptr || chunks_per_lane == nullptr || team_lanes == nullptr)
     return twv::fail(TW_ERR_INVALID_ARG, "output pointer is NULL");
@@ -412,9 +446,10 @@ tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t ro
   if ((hidden * b) % 16 != 0) return twv::fail(TW_ERR_UNSUPPORTED, "row bytes not a multiple of 16");
   if (hidden * b > TW_MAX_HIDDEN_BYTES) return twv::fail(TW_ERR_UNSUPPORTED, "row too wide");
   if (rows < 0) return twv::fail(TW_ERR_INVALID_ARG, "rows must be >= 0");
-  if (cus < 1) return twv::fail(TW_ERR_INVALID_ARG, "cus must be >= 1");
+  if (cus < 1 || device_cus < cus)
+    return twv::fail(TW_ERR_INVALID_ARG, "need 1 <= cus <= device_cus (got %d, %d)", cus, device_cus);
   twv::Shape s{};
-  tw_status st = twv::choose_shape(dtype, hidden, n, rows, cus, &s);
+  tw_status st = twv::choose_shape(dtype, hidden, n, rows, cus, device_cus, &s);
   if (st != TW_OK) return st;
   *waves = s.waves;
   *chunks_per_lane = s.k;

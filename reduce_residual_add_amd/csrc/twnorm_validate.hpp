@@ -39,9 +39,10 @@ tw_status check_copy(const void* src, const void* dst, int64_t bytes, int n_cu_l
 tw_status check_mix(const void* const* srcs, int n_src, const void* const* dsts, int n_dst,
                     int64_t bytes, int n_cu_limit);
 
-// Shape for (dtype, hidden, n) when `rows` rows run on `cus` CUs; honours the
-// tw_set_fused_shape override.
-tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, Shape* shape);
+// Shape for (dtype, hidden, n) when `rows` rows run on `cus` of the device's
+// `device_cus` CUs; honours the tw_set_fused_shape override.
+tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, int device_cus,
+                       Shape* shape);
 
 // True if the wide-row kernel for (dtype, n, waves, k) needs scratch memory
 // (from the build's register-fit table).

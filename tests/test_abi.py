@@ -254,7 +254,13 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 8192, 8, rows=1, cus=256) == (16, 1, 0)
     assert twn.query_fused_shape(BF16, 8192, 8, rows=255, cus=256) == (16, 1, 0)
     assert twn.query_fused_shape(BF16, 8192, 8, rows=256, cus=256) == (4, 4, 0)
-    assert twn.query_fused_shape(BF16, 8192, 8, rows=64, cus=8) == (4, 4, 0)   # CU-limited
+    # on at most half of the CUs: the shapes measured for that regime
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=2048, cus=8) == (8, 2, 0)
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=2048, cus=128) == (8, 2, 0)
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=2048, cus=129) == (4, 4, 0)
+    assert twn.query_fused_shape(BF16, 5120, 4, rows=4096, cus=32) == (10, 1, 0)
+    assert twn.query_fused_shape(BF16, 4096, 2, rows=4096, cus=32) == (8, 1, 0)   # none measured
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=64, cus=8, device_cus=8) == (4, 4, 0)
     assert twn.query_fused_shape(BF16, 5120, 4, rows=8, cus=256) == (10, 1, 0)
     assert twn.query_fused_shape(BF16, 4096, 2, rows=8, cus=256) == (8, 1, 0)
     assert twn.query_fused_shape(BF16, 16384, 2, rows=8, cus=256) == (16, 2, 0)
@@ -263,6 +269,8 @@ def test_shape_choice(lib):
         twn.query_fused_shape(BF16, 8192, 8, rows=-1)
     with pytest.raises(twn.TwError):
         twn.query_fused_shape(BF16, 8192, 8, rows=4, cus=0)
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(BF16, 8192, 8, rows=4, cus=300, device_cus=256)
     with pytest.raises(twn.TwError):
         twn.query_fused_shape(BF16, 12, 2)
     with pytest.raises(twn.TwError):

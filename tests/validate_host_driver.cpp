@@ -72,7 +72,7 @@ int main() {
   for (int n = 1; n <= 16; ++n)
     for (int64_t h = 8; h <= 65536; h += 8) {
       twv::Shape s{};
-      if (twv::choose_shape(TW_BF16, h, n, (h & 64) ? 1 : 4096, 256, &s) != TW_OK) { ++failures; break; }
+      if (twv::choose_shape(TW_BF16, h, n, (h & 64) ? 1 : 4096, (h & 128) ? 8 : 256, 256, &s) != TW_OK) { ++failures; break; }
       const int64_t chunks = h * 2 / 16;
       if (s.k == 0 ? (s.team < chunks || s.team > 32) : ((int64_t)s.waves * 64 * s.k < chunks || s.waves > 16)) {
         std::printf("bad shape for h=%lld n=%d\n", (long long)h, n);
