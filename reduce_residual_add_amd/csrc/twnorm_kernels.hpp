@@ -12,8 +12,9 @@
 //           the next row's loads are in flight while this row finishes
 //   sum     s = p_0 + ... + p_{N-1} in index order, x = r + s   (float32)
 //   store   residual_out = round(x)            (the X = X + Y update)
-//   reduce  sum of x^2: per lane -> DPP / ds_swizzle butterfly inside the
-//           wavefront -> LDS across the wavefronts of the row
+//   reduce  sum of x^2: per 16-byte chunk -> one DPP / ds_swizzle butterfly
+//           per group of 64 consecutive chunks -> the group sums in row
+//           order through LDS (an order fixed by the row width alone)
 //   store   out = round(x * rsqrt(ss / H + eps) * w)
 //
 // The pages' kernel sums the N peers inside the switch fabric with 16-byte
@@ -63,7 +64,7 @@ struct F32 {
 };
 
 // ---------------------------------------------------------------------------
-// Streaming memory access through plain pointers (narrow-row, reduce and copy
+// Streaming memory access through plain pointers (the narrow-row and copy
 // kernels).  Partials, residual and outputs are touched once per call, so
 // they carry the non-temporal hint (measured on MI355X: +15-20% HBM
 // throughput over default caching).  TW_NT_LOADS / TW_NT_STORES = 0 select
@@ -348,7 +349,10 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 // Narrow rows (at most 32 chunks): a team of `team` lanes (power of two) per
 // row, 256 / team rows per 256-thread workgroup, one chunk per lane.  The
 // loop bound depends on blockIdx only, so whole wavefronts iterate together
-// and the butterfly always sees every lane active.
+// and the butterfly always sees every lane active.  The row is one 64-chunk
+// group whose lanes past `chunks` hold zeros, and the team butterfly is the
+// first levels of the wide kernel's 64-lane one (the levels above add exact
+// zeros), so both kernels give the same bits for the same row.
 // ---------------------------------------------------------------------------
 template <class D, int N>
 __global__ void __launch_bounds__(256)
