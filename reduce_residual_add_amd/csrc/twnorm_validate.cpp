@@ -276,6 +276,11 @@ static const TunedShape kTuned[] = {
     {2, 1024, 1, 3, 8, 2},   // 8192 bf16 features, few partials
     {2, 512, 1, 3, 8, 1},    // 4096 bf16 features, few partials
     {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
+    {2, 896, 1, 3, 7, 2},    // 7168 bf16 features, few partials (+4% over 4 x 4)
+    {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials (+4% over 4 x 6)
+    {2, 1536, 7, 16, 6, 4},  // 12288 bf16 features, many partials (+2% over 4 x 6)
+    {2, 2048, 1, 3, 16, 2},  // 16384 bf16 features, few partials (+2% over 4 x 8)
+    {2, 2048, 4, 6, 16, 2},  // 16384 bf16 features, 4-6 partials (+5% over 4 x 8)
 };
 
 // Shapes measured fastest when a call runs on at most half of the CUs: on 8,

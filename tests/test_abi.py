@@ -243,6 +243,9 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 8192, 8) == (4, 4, 0)     # measured shapes
     assert twn.query_fused_shape(BF16, 8192, 2) == (8, 2, 0)
     assert twn.query_fused_shape(BF16, 8192, 4) == (4, 4, 0)
+    assert twn.query_fused_shape(BF16, 7168, 2) == (7, 2, 0)
+    assert twn.query_fused_shape(BF16, 16384, 4) == (16, 2, 0)
+    assert twn.query_fused_shape(BF16, 16384, 8) == (4, 8, 0)
     assert twn.query_fused_shape(BF16, 4096, 2) == (8, 1, 0)
     assert twn.query_fused_shape(BF16, 5120, 4) == (8, 2, 0)
     assert twn.query_fused_shape(BF16, 2048, 2) == (4, 1, 0)     # 4 waves, fewest slots

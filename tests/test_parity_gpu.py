@@ -76,6 +76,10 @@ SHAPES = [
     (3, 13, 12288, "f32"),    # 3072 chunks, fp32
     (2, 3, 65536, "bf16"),    # the widest supported row
     (9, 1, 1024, "bf16"),     # a single row
+    (2, 9, 7168, "bf16"),     # the measured shapes of other common widths
+    (2, 5, 12288, "bf16"),
+    (8, 3, 12288, "bf16"),
+    (4, 3, 16384, "bf16"),
     (16, 2, 65536, "bf16"),   # the most partials on the widest row (every shape spills)
     (4, 3, 32768, "f32"),     # the widest fp32 row
 ]
