@@ -646,3 +646,37 @@ def test_concurrent_host_threads(twn):
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a thread did not finish"
     assert not errors, errors
+
+
+# ---------------------------------------------------------------------------
+# A seeded sweep of random configurations: partial count, dtype, width (any
+# multiple of 16 bytes up to the widest row), row count and in-place use,
+# each checked element by element against the oracle.
+# ---------------------------------------------------------------------------
+def _random_configs(count=120, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        dtype = "bf16" if rng.random() < 0.75 else "f32"
+        per_chunk = 8 if dtype == "bf16" else 4
+        max_chunks = (64 * 1024 if dtype == "bf16" else 32 * 1024) // per_chunk
+        # widths spread over every scale: mostly up to 2048 chunks, some wider
+        top = max_chunks if rng.random() < 0.15 else 2048
+        chunks = int(np.exp(rng.uniform(0, np.log(top))))
+        out.append((int(rng.integers(1, 17)), int(rng.integers(1, 49)),
+                    max(1, chunks) * per_chunk, dtype, bool(rng.random() < 0.3)))
+    return out
+
+
+RANDOM_CASES = _random_configs()
+
+
+def test_fused_random_configs(twn):
+    _say(f"[random configs] {len(RANDOM_CASES)} cases")
+    for i, (n, rows, hidden, dtype, in_place) in enumerate(RANDOM_CASES):
+        _say(f"  case {i}: n={n} rows={rows} H={hidden} {dtype} in_place={in_place}")
+        inp = workloads.make_random(n, rows, hidden, dtype, seed=10_000 + i)
+        out, res_out = _run_fused(twn, inp, in_place=in_place)
+        ref_out, ref_res = O.fused_from_storage(inp)
+        assert_parity(res_out, ref_res, dtype, f"case {i} residual_out")
+        assert_parity(out, ref_out, dtype, f"case {i} out")
