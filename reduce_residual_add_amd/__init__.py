@@ -164,9 +164,15 @@ def _check_tensor(t, name: str, shape, dt, device) -> None:
 
 
 def _stream_ptr(stream=None) -> int:
+    """The hipStream_t of `stream`, else of the current device's current
+    stream (read without building a Stream object when torch offers it)."""
+    if stream is not None:
+        return int(stream.cuda_stream)
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return int(s.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(torch._C._cuda_getDevice()))
+    return int(torch.cuda.current_stream().cuda_stream)
 
 
 def _rows_hidden(t):
@@ -177,7 +183,28 @@ def _rows_hidden(t):
 
 def _check_fused_tensors(partials, residual, weight, out, residual_out):
     """Device, dtype, shape and contiguity of a fused call's tensors; returns
-    (rows, hidden, n)."""
+    (rows, hidden, n).  One combined test per tensor on the common path; the
+    per-property checks below run only to word the error."""
+    shape = residual.shape
+    n = len(partials)
+    if len(shape) == 2 and residual.is_cuda and 1 <= n <= TW_MAX_PARTIALS:
+        dt, dev = residual.dtype, residual.get_device()
+        wshape = shape[1:]
+        ok = residual.is_contiguous() and (
+            weight.is_cuda and weight.dtype is dt and weight.get_device() == dev and
+            weight.shape == wshape and weight.is_contiguous())
+        if ok:
+            for t in (out, residual_out, *partials):
+                if not (t.is_cuda and t.dtype is dt and t.get_device() == dev and t.shape == shape
+                        and t.is_contiguous()):
+                    ok = False
+                    break
+        if ok:
+            return int(shape[0]), int(shape[1]), n
+    return _check_fused_tensors_slow(partials, residual, weight, out, residual_out)
+
+
+def _check_fused_tensors_slow(partials, residual, weight, out, residual_out):
     rows, hidden = _rows_hidden(residual)
     dt, dev = residual.dtype, residual.device
     n = len(partials)
@@ -190,6 +217,16 @@ def _check_fused_tensors(partials, residual, weight, out, residual_out):
     _check_tensor(out, "out", (rows, hidden), dt, dev)
     _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
     return rows, hidden, n
+
+
+_DTYPE_CODES = {}
+
+
+def _dtype_code_fast(t) -> int:
+    c = _DTYPE_CODES.get(t.dtype)
+    if c is None:
+        c = _DTYPE_CODES[t.dtype] = dtype_code(t)
+    return c
 
 
 # ---------------------------------------------------------------------------
@@ -212,7 +249,7 @@ def fused_reduce_rmsnorm(partials: Sequence, residual, weight, eps: float, *, ou
     if rows == 0:   # nothing to do (an empty tensor's data_ptr() may be NULL)
         return out, residual_out
     arr = (_vp * n)(*[p.data_ptr() for p in partials])
-    _check(lib.tw_fused_reduce_rmsnorm(arr, n, rows, hidden, dtype_code(residual),
+    _check(lib.tw_fused_reduce_rmsnorm(arr, n, rows, hidden, _dtype_code_fast(residual),
                                        residual.data_ptr(), weight.data_ptr(), float(eps),
                                        out.data_ptr(), residual_out.data_ptr(), int(n_cu_limit),
                                        _stream_ptr(stream)))

@@ -680,3 +680,31 @@ def test_fused_random_configs(twn):
         ref_out, ref_res = O.fused_from_storage(inp)
         assert_parity(res_out, ref_res, dtype, f"case {i} residual_out")
         assert_parity(out, ref_out, dtype, f"case {i} out")
+
+
+# ---------------------------------------------------------------------------
+# The binding refuses mismatched GPU tensors before anything is enqueued.
+# ---------------------------------------------------------------------------
+def test_binding_rejects_mismatched_tensors(twn):
+    import torch
+    _say("[binding] mismatched tensors")
+    inp = workloads.make_random(3, 8, 1024, "bf16", seed=5)
+    parts, res, wt = inputs_to_dev(inp)
+    out = torch.zeros_like(res)
+    bad = [
+        dict(partials=[parts[0], parts[1].float(), parts[2]]),                  # dtype
+        dict(partials=[parts[0], parts[1][:4], parts[2]]),                       # shape
+        dict(partials=[parts[0], parts[1].t().contiguous().t(), parts[2]]),      # layout
+        dict(weight=wt[:512]),                                                   # weight shape
+        dict(weight=wt.float()),                                                 # weight dtype
+        dict(residual_out=torch.zeros(8, 1024, dtype=torch.bfloat16)),           # host tensor
+        dict(partials=[]),                                                       # no partials
+    ]
+    for i, kw in enumerate(bad):
+        args = dict(partials=parts, residual=res, weight=wt, out=out, residual_out=None)
+        args.update(kw)
+        with pytest.raises((ValueError, TypeError)):
+            twn.fused_reduce_rmsnorm(args["partials"], args["residual"], args["weight"], 1e-5,
+                                     out=args["out"], residual_out=args["residual_out"])
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(out)) == 0
