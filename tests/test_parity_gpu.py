@@ -708,3 +708,40 @@ def test_binding_rejects_mismatched_tensors(twn):
                                      out=args["out"], residual_out=args["residual_out"])
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(out)) == 0
+
+
+def test_concurrent_threads_with_cu_limits(twn):
+    """Three host threads issue CU-limited calls (8, 16 and 32 CUs: masked
+    streams created and joined concurrently) on their own streams; every
+    result is bit-identical to the whole-chip result."""
+    import threading
+    import torch
+    _say("[threads] CU-limited calls from 3 threads")
+    inp = workloads.make_random(8, 96, 8192, "bf16", seed=77)
+    parts, res, wt = inputs_to_dev(inp)
+    o_ref, r_ref = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    torch.cuda.synchronize()
+    ref = (from_dev(o_ref, "bf16"), from_dev(r_ref, "bf16"))
+    errors = []
+
+    def worker(cu):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], n_cu_limit=cu)
+                        for _ in range(10)]
+            s.synchronize()
+            for o, r in outs:
+                if not (np.array_equal(from_dev(o, "bf16"), ref[0]) and np.array_equal(from_dev(r, "bf16"), ref[1])):
+                    errors.append(f"cu {cu}: result differs")
+                    return
+        except Exception as e:  # reported below
+            errors.append(f"cu {cu}: {e!r}")
+
+    threads = [threading.Thread(target=worker, args=(cu,)) for cu in (8, 16, 32)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors
