@@ -252,10 +252,14 @@ tw_status tw_reduce(const void* const* partials, int n, int64_t rows, int64_t hi
   for (int i = 0; i < n; ++i) pp.p[i] = static_cast<const twk::u32x4*>(partials[i]);
   const int64_t total = rows * (hidden * twv::elem_bytes(dtype) / 16);
   auto* red = static_cast<twk::u32x4*>(reduced);
+  int cus = 0;
+  st = current_device_cus(&cus);
+  if (st != TW_OK) return st;
   return run(n_cu_limit, static_cast<hipStream_t>(stream), "reduce kernel launch",
              [&](int cu, hipStream_t s) {
-               return dtype == TW_BF16 ? twl::launch_reduce_bf16(n, pp, red, total, cu, s)
-                                       : twl::launch_reduce_f32(n, pp, red, total, cu, s);
+               const int grid_cus = cu > 0 ? cu : cus;
+               return dtype == TW_BF16 ? twl::launch_reduce_bf16(n, pp, red, total, grid_cus, s)
+                                       : twl::launch_reduce_f32(n, pp, red, total, grid_cus, s);
              });
 }
 

@@ -9,8 +9,8 @@ hipError_t launch_fused_bf16_n1to8(const Launch& L, const FusedArgs& a, hipStrea
 }
 
 hipError_t launch_reduce_bf16(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
-                              int64_t total_chunks, int cu_limit, hipStream_t s) {
-  return detail::reduce<twk::Bf16>(n, pp, reduced, total_chunks, cu_limit, s);
+                              int64_t total_chunks, int grid_cus, hipStream_t s) {
+  return detail::reduce<twk::Bf16>(n, pp, reduced, total_chunks, grid_cus, s);
 }
 
 }  // namespace twl

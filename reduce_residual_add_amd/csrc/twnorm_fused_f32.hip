@@ -97,8 +97,8 @@ hipError_t launch_fused_f32_n1to8(const Launch& L, const FusedArgs& a, hipStream
 }
 
 hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
-                             int64_t total_chunks, int cu_limit, hipStream_t s) {
-  return detail::reduce<twk::F32>(n, pp, reduced, total_chunks, cu_limit, s);
+                             int64_t total_chunks, int grid_cus, hipStream_t s) {
+  return detail::reduce<twk::F32>(n, pp, reduced, total_chunks, grid_cus, s);
 }
 
 hipError_t launch_mix(int n_src, const twk::MixPtrs& m, int64_t bytes, int persistent_cus,

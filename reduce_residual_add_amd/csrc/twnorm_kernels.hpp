@@ -394,35 +394,64 @@ fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 }
 
 // ---------------------------------------------------------------------------
-// Unfused comparison path, first kernel: reduced = round(sum_i p_i), a flat
-// grid-stride loop over 16-byte chunks (the reduce half of a ReduceScatter
-// written to HBM).  It uses the same buffer addressing and cache policy as
-// the fused kernel, so the comparison measures the HBM round trip of the
-// intermediate and nothing else: each block-step gets descriptors based at
-// its first chunk and sized to the chunks left, and lanes past the end load
-// zeros and have their stores dropped.
+// Unfused comparison path, first kernel: reduced = round(sum_i p_i), the
+// reduce half of a ReduceScatter written to HBM.  It walks the tensors in
+// blocks of 256 lanes x K chunk slots with the fused kernel's access order,
+// cache policy and pipelining (this block's result stored, then the next
+// block's loads issued) on a persistent grid of 2 workgroups per CU, so the
+// comparison measures the HBM round trip of the intermediate and nothing
+// else.  A block's descriptors cover only the chunks left: lanes past the end
+// load zeros and have their stores dropped.
 // ---------------------------------------------------------------------------
+template <int N>
+constexpr int reduce_slots() { return N <= 8 ? 4 : 2; }
+
+template <int N>
+__device__ __forceinline__ void reduce_load(u32x4 (&raw)[reduce_slots<N>()][N],
+                                            const PartialPtrs& pp, int64_t first_chunk,
+                                            int bytes, unsigned lane_off) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const rsrc_t r = make_rsrc(pp.p[i] + first_chunk, bytes);
+#pragma unroll
+    for (int k = 0; k < reduce_slots<N>(); ++k) raw[k][i] = buf_load(r, lane_off + k * 4096u);
+  }
+}
+
 template <class D, int N>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 reduce_kernel(PartialPtrs pp, u32x4* reduced, int64_t total_chunks) {
   constexpr int E = D::kElems;
+  constexpr int K = reduce_slots<N>();
+  constexpr int64_t kBlock = 256 * K;  // chunks per block
   const unsigned lane_off = threadIdx.x * 16u;
-  const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b0 = (int64_t)blockIdx.x * blockDim.x; b0 < total_chunks; b0 += step) {
-    const int64_t left = total_chunks - b0;
-    const int bytes = int(left < int64_t(blockDim.x) ? left : int64_t(blockDim.x)) * 16;
-    u32x4 raw[N];
+  const int64_t blocks = (total_chunks + kBlock - 1) / kBlock;
+  auto bytes_of = [&](int64_t b) {
+    const int64_t left = total_chunks - b * kBlock;
+    return int(left < kBlock ? left : kBlock) * 16;
+  };
+  u32x4 raw[K][N];
+  int64_t b = blockIdx.x;
+  if (b < blocks) reduce_load<N>(raw, pp, b * kBlock, bytes_of(b), lane_off);
+  for (; b < blocks; b += gridDim.x) {
+    u32x4 o[K];
 #pragma unroll
-    for (int i = 0; i < N; ++i) raw[i] = buf_load(make_rsrc(pp.p[i] + b0, bytes), lane_off);
-    float acc[E], t[E];
-    widen(D{}, raw[0], acc);
+    for (int k = 0; k < K; ++k) {
+      float acc[E], t[E];
+      widen(D{}, raw[k][0], acc);
 #pragma unroll
-    for (int i = 1; i < N; ++i) {
-      widen(D{}, raw[i], t);
+      for (int i = 1; i < N; ++i) {
+        widen(D{}, raw[k][i], t);
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += t[e];
+        for (int e = 0; e < E; ++e) acc[e] += t[e];
+      }
+      o[k] = narrow(D{}, acc);
     }
-    buf_store(narrow(D{}, acc), make_rsrc(reduced + b0, bytes), lane_off);
+    const rsrc_t r = make_rsrc(reduced + b * kBlock, bytes_of(b));
+#pragma unroll
+    for (int k = 0; k < K; ++k) buf_store(o[k], r, lane_off + k * 4096u);
+    const int64_t next = b + gridDim.x;
+    if (next < blocks) reduce_load<N>(raw, pp, next * kBlock, bytes_of(next), lane_off);
   }
 }
 

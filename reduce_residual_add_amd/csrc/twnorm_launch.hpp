@@ -41,10 +41,11 @@ inline hipError_t launch_fused(bool bf16, const Launch& L, const FusedArgs& a, h
   if (bf16) return L.n <= 8 ? launch_fused_bf16_n1to8(L, a, s) : launch_fused_bf16_n9to16(L, a, s);
   return L.n <= 8 ? launch_fused_f32_n1to8(L, a, s) : launch_fused_f32_n9to16(L, a, s);
 }
+// grid_cus: CUs of the persistent grid (the CU limit, else the device's)
 hipError_t launch_reduce_bf16(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
-                              int64_t total_chunks, int cu_limit, hipStream_t s);
+                              int64_t total_chunks, int grid_cus, hipStream_t s);
 hipError_t launch_reduce_f32(int n, const twk::PartialPtrs& pp, twk::u32x4* reduced,
-                             int64_t total_chunks, int cu_limit, hipStream_t s);
+                             int64_t total_chunks, int grid_cus, hipStream_t s);
 hipError_t launch_copy(const twk::u32x4* src, twk::u32x4* dst, int64_t chunks, int cu_limit,
                        hipStream_t s);
 // persistent_cus: CUs of the persistent grid (the CU limit, else the device's)

@@ -127,7 +127,10 @@ hipError_t fused_range(const Launch& L, const FusedArgs& a, hipStream_t s) {
 template <class D, int N>
 hipError_t reduce_n(const twk::PartialPtrs& pp, twk::u32x4* reduced, int64_t total, int cu_limit,
                     hipStream_t s) {
-  return go(twk::reduce_kernel<D, N>, 256, (total + 255) / 256, cu_limit, s, pp, reduced, total);
+  // cu_limit here is the persistent grid's CU count (the limit, else the device's)
+  constexpr int64_t block = 256 * twk::reduce_slots<N>();
+  return go_capped(twk::reduce_kernel<D, N>, 256, (total + block - 1) / block, cu_limit, 2, s, pp,
+                   reduced, total);
 }
 
 template <class D>
