@@ -7,9 +7,12 @@ for bf16, <= 1e-5 relative for fp32"):
   fp32: element passes iff |got - ref| <= 1e-5 * max(1, |ref|)
 The literal conjunction cannot hold for any correct kernel: a relative bound
 is meaningless at |ref| ~ 0, and one bf16 half-ulp above 8 is 0.031 > 2e-2.
-Every bf16 result is also checked to lie within one bf16 ulp of the oracle's
-correctly rounded value (float32 accumulation error is far below half an
-ulp, so only rounding-boundary cases may differ by one), and in every
+Every bf16 result of at least 1/256 of the array's largest magnitude is also
+checked to lie within one bf16 ulp of the oracle's correctly rounded value
+(float32 accumulation error is far below half an ulp there, so only
+rounding-boundary cases may differ by one; tinier results can sit next to a
+cancellation, where float32 order legitimately moves them by several ulps at
+~1e-8 absolute), and in every
 comparison of at least 4096 outputs at least 99.9% of them must be exactly
 that correctly rounded value (the chance that float32 error crosses a bf16
 rounding boundary is of order 1e-4 per output).
@@ -59,7 +62,15 @@ def tolerance_report(got_storage, ref, dtype):
     if dtype == "bf16":
         rne = O.bf16_encode_rne(ref)
         dist = bf16_ulp_distance(got_storage, rne)
-        rep["max_ulp"] = int(dist.max()) if d.size else 0
+        # The one-ulp bound holds where float32 rounding is far below half a
+        # bf16 ulp.  Near a cancellation (|ref| much smaller than the terms
+        # summed) the specified float32 order can move a tiny result by
+        # several ulps at ~1e-8 absolute, so those elements are left to the
+        # tolerance above.
+        mag = np.abs(ref)
+        well = mag >= (mag.max() / 256.0 if mag.size else 0.0)
+        rep["max_ulp"] = int(dist[well].max()) if np.any(well) else 0
+        rep["max_ulp_all"] = int(dist.max()) if d.size else 0
         # share of outputs that are exactly the correctly rounded value
         rep["exact_frac"] = float(np.count_nonzero(dist == 0) / dist.size) if d.size else 1.0
         rep["n"] = int(d.size)

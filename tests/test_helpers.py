@@ -22,3 +22,23 @@ def test_tolerance_reading():
     f = np.array([1e-6, 2.0], np.float32)
     assert tolerance_report(f, np.array([0.0, 2.0 + 1.9e-5]), "f32")["fails"] == 0
     assert tolerance_report(f, np.array([2e-5, 2.0]), "f32")["fails"] == 1
+
+
+def test_cancellation_moves_tiny_results_by_several_ulps():
+    """Why the one-ulp check skips results far below the array's magnitude:
+    summing in float32 in index order (the kernel's specified arithmetic)
+    next to a cancellation legitimately lands several bf16 ulps from the
+    correctly rounded exact sum, at ~1e-8 absolute."""
+    import numpy as np
+    from oracle import twnorm_oracle as O
+    terms = [-1.1875, 0.8828125, -1.555308699607849e-07, 0.3046875]   # bf16-exact values
+    for t in terms:
+        assert O.bf16_decode(O.bf16_encode_rne(np.array([t])))[0] == t
+    s32 = np.float32(0.0)
+    for t in terms:
+        s32 = np.float32(s32 + np.float32(t))
+    exact = sum(terms)
+    ulps = bf16_ulp_distance(O.bf16_encode_rne(np.array([float(s32)])),
+                             O.bf16_encode_rne(np.array([exact])))[0]
+    assert ulps == 7
+    assert abs(float(s32) - exact) < 1e-8
