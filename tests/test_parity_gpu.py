@@ -745,3 +745,21 @@ def test_concurrent_threads_with_cu_limits(twn):
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a thread did not finish"
     assert not errors, errors
+
+
+@pytest.mark.parametrize("nbytes,cu", [(16, 0), (4096 + 16, 0), ((1 << 20) + 48, 0), ((3 << 20) + 4080, 8)],
+                         ids=["16B", "4KiB+16", "1MiB+48", "3MiB+4080-cu8"])
+def test_stream_copy_copies_bytes(twn, nbytes, cu):
+    """The plain-copy measurement aid (used to scale the hardware counters)
+    copies every byte and nothing past the end."""
+    import torch
+    _say(f"[stream copy] bytes={nbytes} n_cu_limit={cu}")
+    rng = np.random.default_rng(nbytes)
+    src_h = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    src = torch.from_numpy(src_h).cuda()
+    full = torch.full((nbytes + 256,), 7, dtype=torch.uint8, device="cuda")
+    twn.stream_copy(src, full[:nbytes], n_cu_limit=cu)
+    torch.cuda.synchronize()
+    got = full.cpu().numpy()
+    assert np.array_equal(got[:nbytes], src_h)
+    assert (got[nbytes:] == 7).all()
