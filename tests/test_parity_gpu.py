@@ -763,3 +763,20 @@ def test_stream_copy_copies_bytes(twn, nbytes, cu):
     got = full.cpu().numpy()
     assert np.array_equal(got[:nbytes], src_h)
     assert (got[nbytes:] == 7).all()
+
+
+def test_grid_cap_changes_no_bit(twn):
+    """Capping the persistent grid (1 or 2 workgroups per CU, so each
+    workgroup walks more rows) changes no result bit."""
+    import torch
+    _say("[grid cap] 1 and 2 workgroups per CU")
+    inp = workloads.make_random(8, 700, 8192, "bf16", seed=31)
+    ref_out, ref_res = _run_fused(twn, inp)
+    for cap in (1, 2):
+        twn.set_fused_shape(0, 0, cap)
+        try:
+            out, res_out = _run_fused(twn, inp)
+        finally:
+            twn.set_fused_shape(0, 0, 0)
+        assert np.array_equal(out, ref_out) and np.array_equal(res_out, ref_res), f"cap {cap}"
+    torch.cuda.synchronize()
