@@ -88,6 +88,9 @@ def parse_args(argv=None):
     p.add_argument("--unfused-steps", type=int, default=0,
                    help="after the timed steps, run this many unfused reduce + norm pairs "
                         "(for hardware-counter runs)")
+    p.add_argument("--allgather-steps", type=int, default=0,
+                   help="after the timed steps, run this many fused calls with the AllGather "
+                        "store into N gather buffers (for hardware-counter runs)")
     p.add_argument("--calibration-copies", type=int, default=0,
                    help="after the timed steps, run this many plain copies of "
                         f"{COPY_CAL_BYTES >> 20} MiB (hardware-counter calibration)")
@@ -549,6 +552,16 @@ def main(argv=None):
             twn.reduce(d["parts"], out=d["red"])
             twn.rmsnorm(d["red"], d["res"], d["w"], w.eps, out=d["out"], residual_out=d["res_out"])
         torch.cuda.synchronize()
+
+    if args.allgather_steps > 0:
+        gathers = [torch.empty((w.n * w.rows, w.hidden), dtype=sets[0]["res"].dtype, device="cuda")
+                   for _ in range(w.n)]
+        for i in range(args.allgather_steps):
+            d = sets[i % len(sets)]
+            twn.fused_reduce_rmsnorm_allgather(d["parts"], d["res"], d["w"], w.eps, gathers,
+                                               (i % w.n) * w.rows, residual_out=d["res_out"])
+        torch.cuda.synchronize()
+        del gathers
 
     if args.calibration_copies > 0:
         src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
