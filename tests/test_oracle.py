@@ -201,8 +201,79 @@ def check_invariants(oracle) -> str | None:
     return None
 
 
+def _bf16_bits_by_hand(values) -> np.ndarray:
+    """bf16 storage of values that bf16 holds exactly: the high half of the
+    float32 bit pattern (asserting the low half is zero, i.e. no rounding)."""
+    bits32 = np.asarray(values, dtype=np.float32).view(np.uint32)
+    assert np.all((bits32 & 0xFFFF) == 0), "value is not bf16-exact"
+    return (bits32 >> 16).astype(np.uint16)
+
+
+def _storage_case(case, dtype) -> dict:
+    """A golden case as a ``workloads.make``-style storage dict."""
+    store = _bf16_bits_by_hand if dtype == "bf16" else (lambda v: np.asarray(v, dtype=np.float32))
+    res = np.array(case["residual"], dtype=np.float64)
+    return dict(partials=[store(p) for p in case["partials"]], residual=store(res),
+                weight=store(case["weight"]), eps=case["eps"], dtype=dtype,
+                n=len(case["partials"]), rows=res.shape[0], hidden=res.shape[1])
+
+
+def check_storage_wrappers(oracle) -> str | None:
+    """The wrappers on stored bits (what every GPU comparison calls) give the
+    hand-derived golden values in both storage formats: fused_from_storage
+    on the stored inputs, and rmsnorm_from_storage on the stored sum of the
+    partials (every golden sum is exact in both formats)."""
+    for case in _golden()["cases"]:
+        want_res = np.array(case["residual_out"], dtype=np.float64)
+        want_out = np.array(case["out"], dtype=np.float64)
+        for dt in ("bf16", "f32"):
+            inp = _storage_case(case, dt)
+            out, res = oracle.fused_from_storage(inp)
+            if not np.array_equal(res, want_res):
+                return f"fused_from_storage {case['name']} {dt}: residual_out {res}"
+            if not np.allclose(out, want_out, rtol=1e-15, atol=1e-15):
+                return f"fused_from_storage {case['name']} {dt}: out {out}"
+            summed = want_res - np.array(case["residual"], dtype=np.float64)
+            reduced = _bf16_bits_by_hand(summed) if dt == "bf16" else summed.astype(np.float32)
+            out, res = oracle.rmsnorm_from_storage(reduced, inp)
+            if not np.array_equal(res, want_res):
+                return f"rmsnorm_from_storage {case['name']} {dt}: residual_out {res}"
+            if not np.allclose(out, want_out, rtol=1e-15, atol=1e-15):
+                return f"rmsnorm_from_storage {case['name']} {dt}: out {out}"
+    return None
+
+
+def check_eps_as_passed(oracle) -> str | None:
+    """The kernel receives eps as a C float.  float32(0.1) is 13421773 / 2^27
+    and float32(1e-5) is 10995116 / 2^40 (the nearest multiples of 2^-27 and
+    2^-40 with 24 significant bits); 2^-20 is exact.  A constant row
+    2^-10 (mean square 2^-20) with eps = 0.1 then has the exact result
+    2^-10 / sqrt(2^-20 + 13421773 / 2^27) * w, which differs from the result
+    with the float64 eps 0.1 by 7.45e-9 relative: the cast is visible."""
+    for eps, want in ((0.1, Fraction(13421773, 2 ** 27)), (1e-5, Fraction(10995116, 2 ** 40)),
+                      (2.0 ** -20, Fraction(1, 2 ** 20)), (0.0, Fraction(0))):
+        if Fraction(oracle.eps_as_passed(eps)) != want:
+            return f"eps_as_passed({eps}) = {oracle.eps_as_passed(eps)!r}"
+    getcontext().prec = 50
+    ms_plus_eps = Fraction(1, 2 ** 20) + Fraction(13421773, 2 ** 27)
+    root = (Decimal(ms_plus_eps.numerator) / Decimal(ms_plus_eps.denominator)).sqrt()
+    w = [1.0, 0.5, 2.0, 1.5]
+    for dt in ("bf16", "f32"):
+        case = dict(partials=[[[2.0 ** -11] * 4], [[2.0 ** -11] * 4]], residual=[[0.0] * 4],
+                    weight=w, eps=0.1)
+        out, res = oracle.fused_from_storage(_storage_case(case, dt))
+        if not np.array_equal(res, np.full((1, 4), 2.0 ** -10)):
+            return f"eps case {dt}: residual_out {res}"
+        for j in range(4):
+            exact = Decimal(1) / Decimal(1024) / root * Decimal(w[j])
+            if abs(Decimal(float(out[0, j])) - exact) > Decimal("1e-15") * abs(exact):
+                return f"eps case {dt}: out[{j}] {out[0, j]!r} != {exact}"
+    return None
+
+
 ALL_PINS = [check_golden, check_library_special_case, check_brute_force, check_token_split,
-            check_zero_padded_columns, check_closed_forms, check_invariants]
+            check_zero_padded_columns, check_closed_forms, check_invariants,
+            check_storage_wrappers, check_eps_as_passed]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -220,7 +291,8 @@ class _Mutant:
     """A copy of the oracle's public functions with one step replaced."""
 
     def __init__(self, **over):
-        for name in ("fused", "reduce_from_storage", "decode", "allgather_rows"):
+        for name in ("fused", "reduce_from_storage", "decode", "allgather_rows",
+                     "fused_from_storage", "rmsnorm_from_storage", "eps_as_passed"):
             setattr(self, name, getattr(O, name))
         for k, v in over.items():
             setattr(self, k, v)
@@ -271,6 +343,69 @@ MUTANTS["residual_out_is_norm"] = _mutant_residual_out_is_norm
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name):
     m = _Mutant(fused=MUTANTS[name])
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            msg = pin(m)
+        except Exception as e:  # a crash also counts as caught
+            msg = f"raised {e!r}"
+        if msg:
+            failures.append(pin.__name__)
+    assert failures, f"planted mistake {name} passes every pin"
+
+
+# Planted mistakes in the wrappers on stored bits: each must fail a pin.
+def _ffs_swapped_residual_weight(inp):
+    dt = inp["dtype"]
+    return O.fused([O.decode(p, dt) for p in inp["partials"]], O.decode(inp["weight"], dt),
+                   O.decode(inp["residual"], dt), O.eps_as_passed(inp["eps"]))
+
+
+def _ffs_eps_uncast(inp):
+    dt = inp["dtype"]
+    return O.fused([O.decode(p, dt) for p in inp["partials"]], O.decode(inp["residual"], dt),
+                   O.decode(inp["weight"], dt), float(inp["eps"]))
+
+
+def _ffs_wrong_decode(inp):
+    """bf16 bits read as IEEE half precision."""
+    def dec(a, dt):
+        return np.asarray(a).view(np.float16).astype(np.float64) if dt == "bf16" else O.decode(a, dt)
+    dt = inp["dtype"]
+    return O.fused([dec(p, dt) for p in inp["partials"]], dec(inp["residual"], dt),
+                   dec(inp["weight"], dt), O.eps_as_passed(inp["eps"]))
+
+
+def _ffs_first_partial_only(inp):
+    return O.fused_from_storage(dict(inp, partials=inp["partials"][:1]))
+
+
+def _rfs_drops_residual(reduced, inp):
+    dt = inp["dtype"]
+    x = O.decode(reduced, dt)
+    return O.fused([x], np.zeros_like(x), O.decode(inp["weight"], dt), O.eps_as_passed(inp["eps"]))
+
+
+def _rfs_unit_weight(reduced, inp):
+    dt = inp["dtype"]
+    return O.fused([O.decode(reduced, dt)], O.decode(inp["residual"], dt),
+                   np.ones(inp["hidden"]), O.eps_as_passed(inp["eps"]))
+
+
+WRAPPER_MUTANTS = {
+    "fused_from_storage_swaps_residual_and_weight": dict(fused_from_storage=_ffs_swapped_residual_weight),
+    "fused_from_storage_eps_not_cast": dict(fused_from_storage=_ffs_eps_uncast),
+    "fused_from_storage_wrong_bf16_decode": dict(fused_from_storage=_ffs_wrong_decode),
+    "fused_from_storage_first_partial_only": dict(fused_from_storage=_ffs_first_partial_only),
+    "rmsnorm_from_storage_drops_residual": dict(rmsnorm_from_storage=_rfs_drops_residual),
+    "rmsnorm_from_storage_unit_weight": dict(rmsnorm_from_storage=_rfs_unit_weight),
+    "eps_as_passed_keeps_float64": dict(eps_as_passed=lambda eps: float(eps)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(WRAPPER_MUTANTS))
+def test_pins_catch_planted_wrapper_mistake(name):
+    m = _Mutant(**WRAPPER_MUTANTS[name])
     failures = []
     for pin in ALL_PINS:
         try:
