@@ -42,7 +42,8 @@
  *                TW_ERR_UNSUPPORTED  hidden * sizeof(dtype) not a multiple of
  *                                    16, a pointer not 16-byte aligned,
  *                                    hidden beyond TW_MAX_HIDDEN_BYTES bytes,
- *                                    or a fourth distinct n_cu_limit.
+ *                                    a fourth distinct n_cu_limit, or a
+ *                                    CU limit after tw_shutdown().
  *                TW_ERR_ALIAS        an output overlaps an input it may not
  *                                    (rules per entry point below).
  *                TW_ERR_HIP          a HIP runtime call or the launch failed;
@@ -54,8 +55,8 @@
  *              k in [1, CUs) runs the kernel on at most k CUs (persistent grid
  *              on a cached CU-masked stream, ordered after and before `stream`
  *              by events).  Results are bit-identical for every n_cu_limit.
- *              Each distinct CU mask needs a hardware queue of its own for the
- *              life of the process: at most 3 distinct masks (limits k, and
+ *              Each distinct CU mask needs a hardware queue of its own until
+ *              tw_shutdown(): at most 3 distinct masks (limits k, and
  *              complements from tw_cu_complement_stream) per device and
  *              process; a fourth returns TW_ERR_UNSUPPORTED.
  *   Determinism The order of every addition depends only on (dtype, hidden,
@@ -86,7 +87,7 @@ typedef enum {
 
 typedef enum { TW_BF16 = 0, TW_F32 = 1 } tw_dtype;
 
-#define TW_ABI_VERSION 3
+#define TW_ABI_VERSION 4
 #define TW_MAX_PARTIALS 16
 /* Largest supported row: 16 waves x 64 lanes x 8 chunks of 16 bytes. */
 #define TW_MAX_HIDDEN_BYTES (16 * 64 * 8 * 16)
@@ -158,38 +159,9 @@ tw_status tw_rmsnorm(const void* reduced, int64_t rows, int64_t hidden, tw_dtype
                      void* residual_out, int n_cu_limit, void* stream);
 
 /*
- * Measurement aid (not part of the method): dst = src, `bytes` bytes, a
- * plain 16-byte-vector streaming copy used as the practical HBM ceiling and
- * to scale hardware traffic counters.  bytes must be a multiple of 16 and both
- * pointers 16-byte aligned; the ranges may not overlap.
- */
-tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit,
-                         void* stream);
-
-/*
- * Measurement aid (not part of the method): the fused kernel's HBM traffic
- * without its arithmetic, the practical ceiling of that traffic pattern.
- * Reads n_src tensors of `bytes` bytes and writes n_dst tensors of the same
- * size: every 32-bit word of every dst becomes the wrap-around uint32 sum of
- * that word over the srcs.  The access pattern follows the fused kernel's
- * row walk: 16 KiB blocks, each walked by one 256-lane workgroup (4 slots of
- * 16 bytes per lane), the next block's loads issued before this block's
- * stores, and a persistent grid of at most 2 workgroups per CU, with the
- * fused kernel's cache policies (non-temporal loads, device-scope stores).
- * So a fused call over N partials corresponds to n_src = N + 1, n_dst = 2
- * and bytes = rows * hidden * element size.
- * n_src in [1, TW_MAX_PARTIALS + 1], n_dst in [1, TW_MAX_PARTIALS]; bytes a
- * multiple of 16; every pointer 16-byte aligned; no dst may overlap a src or
- * another dst (srcs may overlap each other).  n_cu_limit as for the fused
- * call.  bytes == 0 is a no-op.
- */
-tw_status tw_stream_mix(const void* const* srcs, int n_src, void* const* dsts, int n_dst,
-                        int64_t bytes, int n_cu_limit, void* stream);
-
-/*
  * The library's CU-masked stream for `n_cu_limit` on the current device
- * (created on first use, owned by the library for the life of the process;
- * never destroy it).  Its kernels run only on the CUs of the first
+ * (created on first use and owned by the library until tw_shutdown(); never
+ * destroy it yourself).  Its kernels run only on the CUs of the first
  * n_cu_limit mask bits, which the hardware spreads round-robin over the 8
  * XCDs and then their shader engines.  Calls made on this stream with the
  * same n_cu_limit launch directly, without the per-call event join to the
@@ -209,30 +181,20 @@ tw_status tw_cu_masked_stream(int n_cu_limit, void** stream);
 tw_status tw_cu_complement_stream(int n_cu_limit, void** stream);
 
 /*
- * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts
- * per token row with `chunks_per_lane` 16-byte chunks per lane (both 0 =
- * automatic choice), and cap the persistent grid at `wgs_per_cu` workgroups
- * per CU (0 = as many as the CU holds).  Applies to every later call on every
- * thread; a shape that cannot cover a row returns TW_ERR_UNSUPPORTED at the
- * call.  Neither the shape nor the grid cap changes any result bit: every
- * shape adds in the same order.  Returns TW_ERR_INVALID_ARG for
- * waves outside [0,16], chunks_per_lane not in {0,1,2,3,4,6,8}, only one of
- * the two being 0, or wgs_per_cu < 0.
+ * Ordered teardown of the library's per-device resources: for every device
+ * the library used, waits for the work queued on its CU-masked streams, then
+ * destroys those streams (and their hardware queues) and the two events that
+ * join them to callers' streams.  The HIP runtime must still be alive, so the
+ * library registers this function with atexit() when it creates its first
+ * CU-masked stream (such a handler runs before the runtime's own teardown),
+ * and a caller may call it earlier, e.g. from a language runtime's exit hook.
+ * Idempotent.  Afterwards whole-chip calls keep working, while CU-limited
+ * calls and the two stream queries return TW_ERR_UNSUPPORTED: the queues are
+ * not created a second time.  Streams obtained from tw_cu_masked_stream or
+ * tw_cu_complement_stream are invalid after it.  Returns TW_ERR_HIP if a
+ * synchronisation or destroy call failed (the rest are still released).
  */
-tw_status tw_set_fused_shape(int waves, int chunks_per_lane, int wgs_per_cu);
-
-/* Launch shape the fused kernel would use for (dtype, hidden, n partials)
- * when `rows` rows run on `cus` CUs (the CU limit of the call, else the
- * device's count) of a device with `device_cus` CUs; writes the wavefronts
- * per row and chunks per lane (team_lanes for rows narrower than one
- * wavefront, else 0).  Calls of fewer rows than CUs get as many wavefronts
- * per row as the row fills; calls on at most half of the device's CUs may
- * get a shape measured for that regime instead of the whole-chip one.
- * The results are the same bits for every shape.  Needs
- * 1 <= cus <= device_cus and rows >= 0.  HIP-free. */
-tw_status tw_query_fused_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus,
-                               int device_cus, int* waves, int* chunks_per_lane,
-                               int* team_lanes);
+tw_status tw_shutdown(void);
 
 const char* tw_status_string(tw_status s);
 /* Detail of the last non-OK return on the calling thread ("" if none). */

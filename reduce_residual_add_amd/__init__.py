@@ -6,11 +6,13 @@ kernels of ``libtwnorm.so`` (built in-tree by ``reduce_residual_add_amd.build``)
 PyTorch provides device memory and the current HIP stream.  There is no CPU
 fallback: if the library is missing, every call raises.
 
-The C entry points are declared in ``include/twnorm.h``; the functions below
-carry the same names without the ``tw_`` prefix.
+The C entry points are declared in ``include/twnorm.h`` (the measurement and
+tuning aids in ``include/twnorm_bench.h``); the functions below carry the same
+names without the ``tw_`` prefix.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -21,7 +23,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libtwnorm.so")
 TW_OK, TW_ERR_INVALID_ARG, TW_ERR_UNSUPPORTED, TW_ERR_ALIAS, TW_ERR_HIP = 0, -1, -2, -3, -4
 TW_BF16, TW_F32 = 0, 1
 TW_MAX_PARTIALS = 16
-TW_ABI_VERSION = 3
+TW_ABI_VERSION = 4
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -43,10 +45,10 @@ _STATUS_NAMES = {TW_OK: "TW_OK", TW_ERR_INVALID_ARG: "TW_ERR_INVALID_ARG",
                  TW_ERR_HIP: "TW_ERR_HIP"}
 
 EXPORTED = ("tw_fused_reduce_rmsnorm", "tw_fused_reduce_rmsnorm_allgather", "tw_reduce",
-            "tw_rmsnorm", "tw_stream_copy", "tw_stream_mix",
-            "tw_cu_masked_stream", "tw_cu_complement_stream",
-            "tw_set_fused_shape", "tw_query_fused_shape", "tw_status_string",
-            "tw_last_error", "tw_abi_version")
+            "tw_rmsnorm", "tw_cu_masked_stream", "tw_cu_complement_stream", "tw_shutdown",
+            "tw_status_string", "tw_last_error", "tw_abi_version",
+            # measurement and tuning aids (include/twnorm_bench.h)
+            "tw_stream_copy", "tw_stream_mix", "tw_set_fused_shape", "tw_query_fused_shape")
 
 
 def _hip_runtimes_loaded():
@@ -110,6 +112,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                          _c.POINTER(_c.c_int),
                                          _c.POINTER(_c.c_int), _c.POINTER(_c.c_int)]
     lib.tw_query_fused_shape.restype = _c.c_int
+    lib.tw_shutdown.argtypes = []
+    lib.tw_shutdown.restype = _c.c_int
     lib.tw_status_string.argtypes = [_c.c_int]
     lib.tw_status_string.restype = _c.c_char_p
     lib.tw_last_error.argtypes = []
@@ -118,6 +122,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tw_abi_version.restype = _c.c_int
     if lib.tw_abi_version() != TW_ABI_VERSION:
         raise ImportError(f"libtwnorm ABI {lib.tw_abi_version()} != {TW_ABI_VERSION}")
+    # Release the CU-masked streams while torch and the HIP runtime are fully
+    # alive: Python's exit hooks run before any C-level teardown.
+    atexit.register(lib.tw_shutdown)
     _lib = lib
     return lib
 
@@ -400,9 +407,17 @@ def cu_complement_stream(n_cu_limit: int):
     return torch.cuda.ExternalStream(h.value)
 
 
+def shutdown() -> None:
+    """Release the library's CU-masked streams and events now (it also runs
+    at interpreter exit).  Afterwards CU-limited calls raise; whole-chip
+    calls keep working."""
+    _check(load().tw_shutdown())
+
+
 def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0, wgs_per_cu: int = 0) -> None:
     """Force the fused kernel's launch shape (0, 0 = automatic) and cap its
-    persistent grid at wgs_per_cu workgroups per CU (0 = no cap)."""
+    persistent grid at wgs_per_cu workgroups per CU (0 = no cap), for the
+    calling thread's later calls."""
     _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane), int(wgs_per_cu)))
 
 

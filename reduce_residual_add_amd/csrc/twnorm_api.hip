@@ -1,4 +1,5 @@
-// C-ABI entry points of libtwnorm (declared in include/twnorm.h).
+// C-ABI entry points of libtwnorm (declared in include/twnorm.h, and the
+// measurement aids in include/twnorm_bench.h).
 //
 // Each entry point validates its arguments without touching HIP
 // (twnorm_validate.cpp), picks the launch shape from (dtype, hidden, n) and
@@ -10,11 +11,13 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <vector>
 
 #include "twnorm.h"
+#include "twnorm_bench.h"
 #include "twnorm_launch.hpp"
 #include "twnorm_validate.hpp"
 
@@ -31,6 +34,9 @@ struct DeviceState {
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_dev;
+// Set by tw_shutdown(): the masked streams and events are gone and are not
+// created again.  Guarded by g_mu.
+bool g_shut_down = false;
 
 // Report a failed HIP call.  HIP also keeps the error as the thread's sticky
 // "last error"; it is read back and cleared here so that it cannot surface
@@ -86,6 +92,8 @@ tw_status current_device_cus(int* cus_out) {
   return TW_OK;
 }
 
+void shutdown_at_exit() { (void)tw_shutdown(); }
+
 // CU-masked streams keep the default priority.  Each owns a hardware queue of
 // its own, and a process gets few of them (4 by default, shared with the
 // ordinary streams), so at most kMaxMaskedStreams distinct masks are cached
@@ -103,6 +111,10 @@ tw_status masked_stream(DeviceState& d, int key, hipStream_t* out) {
     *out = it->second;
     return TW_OK;
   }
+  if (g_shut_down)
+    return twv::fail(TW_ERR_UNSUPPORTED,
+                     "tw_shutdown() has released the CU-masked streams; CU-limited calls are "
+                     "no longer available in this process");
   if (d.masked.size() >= kMaxMaskedStreams)
     return twv::fail(TW_ERR_UNSUPPORTED,
                      "CU mask %s%d: this process already uses %zu distinct CU masks (the "
@@ -112,6 +124,14 @@ tw_status masked_stream(DeviceState& d, int key, hipStream_t* out) {
   const int lo = key > 0 ? 0 : -key, hi = key > 0 ? key : d.cus;
   for (int i = lo; i < hi; ++i) mask[i / 32] |= 1u << (i % 32);
   hipStream_t s = nullptr;
+  // The queues must be destroyed while the HIP runtime is still alive: an
+  // atexit handler registered now runs before the runtime's own teardown,
+  // which was registered when the runtime was loaded.
+  static bool registered = false;
+  if (!registered) {
+    registered = true;
+    std::atexit(shutdown_at_exit);
+  }
   hipError_t e = hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data());
   if (e != hipSuccess) return hip_fail(e, "hipExtStreamCreateWithCUMask");
   d.masked[key] = s;
@@ -122,18 +142,24 @@ tw_status masked_stream(DeviceState& d, int key, hipStream_t* out) {
 // Run `launch(cu_limit, stream)` on the whole chip or on a CU-limited stream.
 template <typename F>
 tw_status run(int n_cu_limit, hipStream_t caller, const char* what, F&& launch) {
+  if (n_cu_limit > 0) {
+    int cus = 0;
+    tw_status st = current_device_cus(&cus);
+    if (st != TW_OK) return st;
+    if (n_cu_limit >= cus) n_cu_limit = 0;   // the whole chip
+  }
   if (n_cu_limit == 0) {
     hipError_t e = launch(0, caller);
     return e == hipSuccess ? TW_OK : hip_fail(e, what);
   }
   std::lock_guard<std::mutex> lock(g_mu);
+  if (g_shut_down)
+    return twv::fail(TW_ERR_UNSUPPORTED,
+                     "tw_shutdown() has released the CU-masked streams; CU-limited calls are "
+                     "no longer available in this process");
   DeviceState* d = nullptr;
   tw_status st = device_state(&d);
   if (st != TW_OK) return st;
-  if (n_cu_limit >= d->cus) {
-    hipError_t e = launch(0, caller);
-    return e == hipSuccess ? TW_OK : hip_fail(e, what);
-  }
   hipStream_t ms = nullptr;
   st = masked_stream(*d, n_cu_limit, &ms);
   if (st != TW_OK) return st;
@@ -268,6 +294,9 @@ static tw_status masked_stream_entry(int n_cu_limit, bool complement, void** str
   if (stream == nullptr) return twv::fail(TW_ERR_INVALID_ARG, "stream is NULL");
   if (n_cu_limit < 1) return twv::fail(TW_ERR_INVALID_ARG, "n_cu_limit must be >= 1");
   std::lock_guard<std::mutex> lock(g_mu);
+  if (g_shut_down)
+    return twv::fail(TW_ERR_UNSUPPORTED,
+                     "tw_shutdown() has released the CU-masked streams");
   DeviceState* d = nullptr;
   tw_status st = device_state(&d);
   if (st != TW_OK) return st;
@@ -287,6 +316,30 @@ tw_status tw_cu_masked_stream(int n_cu_limit, void** stream) {
 
 tw_status tw_cu_complement_stream(int n_cu_limit, void** stream) {
   return masked_stream_entry(n_cu_limit, true, stream);
+}
+
+tw_status tw_shutdown(void) {
+  twv::clear_error();
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_shut_down = true;
+  tw_status result = TW_OK;
+  for (auto& dev : g_dev) {
+    DeviceState& d = dev.second;
+    for (auto& m : d.masked) {
+      // wait for the stream's work, then release it and its hardware queue
+      hipError_t e = hipStreamSynchronize(m.second);
+      if (e == hipSuccess) e = hipStreamDestroy(m.second);
+      if (e != hipSuccess) result = hip_fail(e, "releasing a CU-masked stream");
+    }
+    d.masked.clear();
+    for (hipEvent_t* ev : {&d.ev_in, &d.ev_out}) {
+      if (*ev == nullptr) continue;
+      const hipError_t e = hipEventDestroy(*ev);
+      if (e != hipSuccess) result = hip_fail(e, "hipEventDestroy");
+      *ev = nullptr;
+    }
+  }
+  return result;
 }
 
 tw_status tw_stream_copy(const void* src, void* dst, int64_t bytes, int n_cu_limit, void* stream) {

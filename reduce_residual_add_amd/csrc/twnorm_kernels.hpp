@@ -264,10 +264,13 @@ __device__ __forceinline__ void load_row(u32x4 (&raw)[K][N + 1], const PartialPt
   }
 }
 
+// `residual` carries no __restrict__: the in-place update passes the same
+// buffer as `residual_out`, and each lane stores a chunk only after loading
+// it.
 template <class D, int N, int K, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
-fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
-                  const u32x4* __restrict__ weight, OutPtrs outs, u32x4* residual_out,
+fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict__ weight,
+                  OutPtrs outs, u32x4* residual_out,
                   int64_t rows, int chunks, float hidden_f, float eps) {
   constexpr int E = D::kElems;
   __shared__ float red[2][MAXW * K];
@@ -356,8 +359,8 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
 // ---------------------------------------------------------------------------
 template <class D, int N>
 __global__ void __launch_bounds__(256)
-fused_team_kernel(PartialPtrs pp, const u32x4* __restrict__ residual,
-                  const u32x4* __restrict__ weight, OutPtrs outs, u32x4* residual_out,
+fused_team_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict__ weight,
+                  OutPtrs outs, u32x4* residual_out,
                   int64_t rows, int chunks, int team, float hidden_f, float eps) {
   constexpr int E = D::kElems;
   const int tid = threadIdx.x;

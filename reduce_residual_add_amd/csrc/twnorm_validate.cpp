@@ -2,7 +2,6 @@
 #include "twnorm_validate.hpp"
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -14,9 +13,11 @@ namespace {
 
 thread_local char g_err[512] = {0};
 
-std::atomic<int> g_override_waves{0};
-std::atomic<int> g_override_k{0};
-std::atomic<int> g_wgs_per_cu{0};
+// Launch-shape override of tw_set_fused_shape: per host thread, so one
+// thread's tuning never changes another thread's calls.
+thread_local int g_override_waves = 0;
+thread_local int g_override_k = 0;
+thread_local int g_wgs_per_cu = 0;
 
 struct Span {
   uintptr_t lo, hi;  // [lo, hi)
@@ -356,7 +357,7 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
   if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
   if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
   const int64_t chunks = hidden * b / 16;
-  const int ow = g_override_waves.load(), ok = g_override_k.load();
+  const int ow = g_override_waves, ok = g_override_k;
   if (ow > 0 && ok > 0) {
     if ((int64_t)ow * 64 * ok < chunks)
       return fail(TW_ERR_UNSUPPORTED, "forced shape %d waves x %d chunks cannot cover %lld chunks",
@@ -406,19 +407,21 @@ tw_status set_override(int waves, int k, int wgs_per_cu) {
   if (waves < 0 || waves > 16 || !k_ok || ((waves == 0) != (k == 0)) || wgs_per_cu < 0)
     return fail(TW_ERR_INVALID_ARG, "invalid forced shape (%d waves, %d chunks per lane, %d per CU)",
                 waves, k, wgs_per_cu);
-  g_override_waves.store(waves);
-  g_override_k.store(k);
-  g_wgs_per_cu.store(wgs_per_cu);
+  g_override_waves = waves;
+  g_override_k = k;
+  g_wgs_per_cu = wgs_per_cu;
   return TW_OK;
 }
 
-int wgs_per_cu_cap() { return g_wgs_per_cu.load(); }
+int wgs_per_cu_cap() { return g_wgs_per_cu; }
 
 }  // namespace twv
 
 // ---------------------------------------------------------------------------
 // HIP-free exported entry points
 // ---------------------------------------------------------------------------
+#include "twnorm_bench.h"
+
 extern "C" {
 
 const char* tw_status_string(tw_status s) {

@@ -40,7 +40,7 @@ tw_status check_mix(const void* const* srcs, int n_src, const void* const* dsts,
                     int64_t bytes, int n_cu_limit);
 
 // Shape for (dtype, hidden, n) when `rows` rows run on `cus` of the device's
-// `device_cus` CUs; honours the tw_set_fused_shape override.
+// `device_cus` CUs; honours the calling thread's tw_set_fused_shape override.
 tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, int device_cus,
                        Shape* shape);
 
@@ -49,7 +49,8 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
 bool shape_spills(tw_dtype dtype, int n, int waves, int k);
 
 // Force (waves, k) for wide rows ((0, 0) restores the automatic choice) and
-// cap the persistent grid at wgs_per_cu workgroups per CU (0 = no cap).
+// cap the persistent grid at wgs_per_cu workgroups per CU (0 = no cap), for
+// the calling thread's later calls.
 tw_status set_override(int waves, int k, int wgs_per_cu);
 int wgs_per_cu_cap();
 

@@ -1,5 +1,5 @@
 """The C ABI without a GPU: the library loads, exports every function that
-include/twnorm.h declares, and every error path returns its status before
+include/twnorm.h and include/twnorm_bench.h declare, and every error path returns its status before
 any HIP call.  Pointers here are fake, 16-byte aligned addresses that the
 validator compares but never dereferences."""
 import ctypes
@@ -9,7 +9,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "twnorm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("twnorm.h", "twnorm_bench.h")]
 
 import reduce_residual_add_amd as twn  # noqa: E402
 
@@ -20,9 +20,12 @@ MB = 1 << 20
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tw_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(tw_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
     assert "tw_fused_reduce_rmsnorm" in declared and "tw_reduce" in declared
     for name in declared:
-        assert hasattr(lib, name), f"{name} declared in twnorm.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
     assert sorted(twn.EXPORTED) == declared
 
 
@@ -357,3 +360,41 @@ def test_last_error_is_per_thread(lib):
     for tid, msgs in results.items():
         want_status = INV if tid % 2 == 0 else UNS
         assert msgs == {(want_status, True)}, (tid, msgs)
+
+
+def test_shape_override_is_per_thread(lib):
+    """tw_set_fused_shape applies to the calling thread only: another
+    thread's shape choice (and so its calls) is unchanged."""
+    import threading
+    auto = twn.query_fused_shape(BF16, 8192, 8, rows=1024)
+    seen = {}
+    twn.set_fused_shape(2, 8)
+    try:
+        assert twn.query_fused_shape(BF16, 8192, 8, rows=1024) == (2, 8, 0)
+        t = threading.Thread(target=lambda: seen.update(other=twn.query_fused_shape(BF16, 8192, 8,
+                                                                                     rows=1024)))
+        t.start()
+        t.join()
+    finally:
+        twn.set_fused_shape(0, 0)
+    assert seen["other"] == auto
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=1024) == auto
+
+
+def test_shutdown_is_idempotent_and_final():
+    """In a fresh process: tw_shutdown twice returns TW_OK, and afterwards
+    the CU-masked stream queries refuse instead of creating queues again
+    (checked before any HIP call, so no GPU is needed)."""
+    import subprocess
+    import sys
+    code = ("import ctypes, reduce_residual_add_amd as t; L = t.load(); "
+            "a = L.tw_shutdown(); b = L.tw_shutdown(); h = ctypes.c_void_p(); "
+            "c = L.tw_cu_masked_stream(8, ctypes.byref(h)); "
+            "d = L.tw_cu_complement_stream(8, ctypes.byref(h)); "
+            "print(a, b, c, d, t.last_error())")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    a, b, c, d, *msg = r.stdout.strip().splitlines()[-1].split(" ")
+    assert (int(a), int(b), int(c), int(d)) == (OK, OK, UNS, UNS)
+    assert "tw_shutdown" in " ".join(msg)
