@@ -13,7 +13,6 @@ import numpy as np
 import pytest
 
 import workloads
-from oracle import twnorm_oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "reduce_residual_add_amd")
@@ -57,7 +56,7 @@ CASES = [
 @pytest.mark.gpu
 @pytest.mark.parametrize("n,rows,hidden,dtype", CASES, ids=[f"n{a}-r{b}-h{c}-{d}" for a, b, c, d in CASES])
 def test_c_caller_matches_oracle(twn, tmp_path, n, rows, hidden, dtype):
-    from gpu_helpers import assert_parity
+    from gpu_helpers import assert_parity, reference
     exe = build_driver(tmp_path)
     inp = workloads.make_random(n, rows, hidden, dtype, seed=rows * n + 3)
     code = 0 if dtype == "bf16" else 1
@@ -76,6 +75,6 @@ def test_c_caller_matches_oracle(twn, tmp_path, n, rows, hidden, dtype):
     assert "refused as expected: TW_ERR_INVALID_ARG" in r.stderr
     storage = np.uint16 if dtype == "bf16" else np.float32
     got = np.fromfile(dst, dtype=storage).reshape(2, rows, hidden)
-    ref_out, ref_res = O.fused_from_storage(inp)
-    assert_parity(got[1], ref_res, dtype, "residual_out from C")
-    assert_parity(got[0], ref_out, dtype, "out from C")
+    ref_out, ref_res, b_out, b_res = reference(inp)
+    assert_parity(got[1], ref_res, dtype, "residual_out from C", b_res)
+    assert_parity(got[0], ref_out, dtype, "out from C", b_out)
