@@ -8,9 +8,14 @@ Default workload: N=8 partials of [1024, 8192] bf16 (one 8-way shard of
 rotating set of resident buffers; S sets totalling at least twice the 256 MB
 Infinity Cache are cycled so the timed bytes come from HBM, not the cache.
 
-Prints ONE JSON line.  --report PATH also writes a detailed JSON: the
+Prints ONE JSON line.  Besides the headline it carries the per-call
+distribution (median, p10, p90 over ~1 ms batches timed right after the
+headline's steps) and a per_config block: every other
+workload at its full size (the CU-restricted one on 8, 16, 32 CUs and the
+whole chip), each with its oracle check of a row slice, and the unfused
+pair on the headline's buffers.  --report PATH also writes a detailed JSON: the
 unfused pair, the AllGather store, decode-size rows, the two-split overlap
-beside a GEMM, the per-call distribution, row-count scaling, the plain-copy
+beside a GEMM, row-count scaling, the plain-copy
 ceiling, the ceiling of the fused call's own traffic pattern, the same step
 as plain eager PyTorch ops, and a cache-resident figure.
 
@@ -91,6 +96,9 @@ def parse_args(argv=None):
     p.add_argument("--allgather-steps", type=int, default=0,
                    help="after the timed steps, run this many fused calls with the AllGather "
                         "store into N gather buffers (for hardware-counter runs)")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="skip the per_config block (every other workload and CU limit, and "
+                        "the unfused pair, timed in the same run)")
     p.add_argument("--calibration-copies", type=int, default=0,
                    help="after the timed steps, run this many plain copies of "
                         f"{COPY_CAL_BYTES >> 20} MiB (hardware-counter calibration)")
@@ -140,6 +148,46 @@ def n_rotating_sets(set_bytes, requested):
     return s
 
 
+def time_batches(step_fns, est_us_per_call, stream=None, batches=30, batch_ms=1.0):
+    """Per-call time distribution over `batches` batches of back-to-back
+    calls, each batch a whole number of passes over the rotating sets and
+    about `batch_ms` of GPU time, with one event between consecutive batches.
+    An event recorded between two kernels on MI355X costs about 1 us of GPU
+    time (measured: 30.3 -> 31.4 us per call with an event every 3 calls), so
+    the headline mean is timed without them and this pass runs after it, with
+    batches long enough that the events cost about 0.1%."""
+    import torch
+    n = len(step_fns)
+    passes = max(1, int(round(batch_ms * 1e3 / max(est_us_per_call, 1e-3) / n)))
+    calls = passes * n
+    for f in step_fns:
+        f()
+    torch.cuda.synchronize()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    marks[0].record(s)
+    for b in range(batches):
+        for i in range(calls):
+            step_fns[i % n]()
+        marks[b + 1].record(s)
+    torch.cuda.synchronize()
+    per_call = [marks[b].elapsed_time(marks[b + 1]) * 1e3 / calls for b in range(batches)]
+    return batch_distribution(per_call, calls)
+
+
+def batch_distribution(per_call_us, calls_per_batch):
+    """Median, p10 and p90 (nearest rank) of per-call times in microseconds,
+    one value per batch."""
+    v = sorted(per_call_us)
+    if not v:
+        return None
+
+    def pct(q):
+        return round(v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))], 3)
+    return {"batches": len(v), "calls_per_batch": calls_per_batch, "median_us": pct(0.5),
+            "p10_us": pct(0.1), "p90_us": pct(0.9)}
+
+
 def time_steps(step_fns, steps, warmup, stream=None):
     """Warm up, then time exactly `steps` calls between two events recorded
     on the stream the kernels run on (default: the current stream), with a
@@ -176,7 +224,7 @@ def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
     spent = 0.0
     first = None
     start = 0
-    while spent < target_seconds and spent < 30.0:
+    while (done_rows == 0 or spent < target_seconds) and spent < 30.0:
         sl = slice(start, start + chunk)
         sub = dict(inp, partials=[p[sl] for p in inp["partials"]], residual=inp["residual"][sl])
         t0 = time.perf_counter()
@@ -244,39 +292,17 @@ def _from_dev(t, dtype):
 # ---------------------------------------------------------------------------
 
 
-def measure_fused(twn, w, sets, cu, steps, warmup, stream=None):
+def measure_fused(twn, w, sets, cu, steps, warmup, stream=None, with_distribution=False):
     """Per-step time of the fused call.  With cu > 0 and `stream` the
     library's CU-masked stream, the kernels are queued and timed there
-    directly (no per-call join to another stream)."""
+    directly (no per-call join to another stream).  With_distribution adds
+    the per-call distribution over ~1 ms batches from a second pass."""
     fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"],
                              n_cu_limit=cu, stream=stream) for d in sets]
     ms, wall = time_steps(fns, steps, warmup, stream=stream)
+    if with_distribution:
+        return ms, wall, time_batches(fns, ms * 1e3, stream=stream)
     return ms, wall
-
-
-def measure_distribution(twn, w, sets, batches=60):
-    """Per-call times from `batches` batches of len(sets) back-to-back calls,
-    each batch between its own pair of events: median, p10 and p90 (us)."""
-    import torch
-    fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"])
-           for d in sets]
-    for f in fns * 3:
-        f()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(batches)]
-    for a, b in evs:
-        a.record()
-        for f in fns:
-            f()
-        b.record()
-    torch.cuda.synchronize()
-    per_call = sorted(a.elapsed_time(b) * 1e3 / len(fns) for a, b in evs)
-
-    def pct(q):
-        return per_call[min(len(per_call) - 1, int(q * len(per_call)))]
-    return {"batches": batches, "calls_per_batch": len(fns), "median_us": pct(0.5),
-            "p10_us": pct(0.1), "p90_us": pct(0.9)}
 
 
 def measure_unfused(twn, w, sets, steps, warmup):
@@ -482,6 +508,89 @@ def measure_copy(twn, total_bytes, steps, warmup):
     return ms, n
 
 
+# CU limits of the CU-restricted workload's sweep (0 = the whole chip).
+SWEEP_CU_LIMITS = (0, 8, 16, 32)
+
+
+def _steps_for(us_per_call, target_ms=20.0, lo=30, hi=2000):
+    """Timed steps that keep one measurement near `target_ms` of GPU time."""
+    return int(min(hi, max(lo, target_ms * 1e3 / max(us_per_call, 1e-3))))
+
+
+def measure_config(twn, w, seed, cu_limits, dev_cus, cpu_seconds):
+    """One workload at its full size, at each CU limit: per-call time over
+    rotating sets, GB/s, fraction of peak, the per-batch distribution, and
+    the oracle's check of a row slice of the outputs the timed calls left."""
+    import torch
+    import workloads
+    inp = workloads.make(w, seed=seed)
+    n_sets = n_rotating_sets(w.fused_bytes(), 0)
+    launch_bound = w.fused_bytes() < (1 << 20)
+    if launch_bound:
+        # A call this small is bound by launch latency, not HBM: its data
+        # stays cache-resident and more sets would change nothing.
+        n_sets = min(n_sets, 64)
+    sets = make_sets(inp, n_sets)
+    code = twn.TW_BF16 if w.dtype == "bf16" else twn.TW_F32
+    entries = {}
+    for cu in cu_limits:
+        stream = twn.cu_masked_stream(cu) if cu > 0 else None
+        probe, _ = measure_fused(twn, w, sets, cu, 3 * n_sets, n_sets, stream=stream)
+        steps = _steps_for(probe * 1e3)
+        steps -= steps % n_sets
+        ms, _, dist = measure_fused(twn, w, sets, cu, steps, max(n_sets, 10), stream=stream,
+                                    with_distribution=True)
+        gbs = w.fused_bytes() / (ms * 1e-3) / 1e9
+        call_cus = cu if 0 < cu < dev_cus else dev_cus
+        e = {"n_cu_limit": cu, "us_per_call": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+             "frac_of_peak": round(gbs / PEAK_GBS, 4),
+             "token_rows_per_s": round(w.rows / (ms * 1e-3), 1), "steps": steps,
+             "rotating_sets": n_sets, "per_call_distribution": dist,
+             "launch_shape": list(twn.query_fused_shape(code, w.hidden, w.n, w.rows, call_cus,
+                                                        dev_cus))}
+        torch.cuda.synchronize()
+        d0 = sets[0]
+        # the timed calls ended on the last set; set 0 holds the outputs of
+        # one of them at this CU limit
+        cb = cpu_baseline(inp, w, _from_dev(d0["out"], w.dtype), _from_dev(d0["res_out"], w.dtype),
+                          cpu_seconds)
+        e["oracle_parity_rows"] = cb["parity_rows"]
+        e["oracle_parity_fails"] = cb["parity_fails"]
+        e["oracle_parity_max_abs"] = cb["parity_max_abs"]
+        e["cpu_oracle_gbs"] = cb["value"]
+        if launch_bound and cu == 0:
+            e["latency_bound"] = True
+            e["us_per_call_graph_replay"] = round(measure_fused_graph(twn, w, sets) * 1e3, 3)
+        entries[f"cu{cu}"] = e
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "n_partials": w.n, "rows": w.rows, "hidden": w.hidden,
+            "dtype": w.dtype, "algorithmic_bytes_per_call": w.fused_bytes(),
+            "traffic_per_call": counter_traffic(w.name), "by_cu_limit": entries}
+
+
+def measure_per_config(twn, args, w_main, main_sets, main_ms, dev_cus):
+    """Every other workload (and the CU-restricted sweep) timed in the same
+    run as the headline, plus the unfused pair on the headline's buffers."""
+    import workloads
+    out = {}
+    # The sweep needs three CU masks of its own; a process may hold three.
+    cu_ok = args.cu == 0 and not args.report
+    for w in workloads.WORKLOADS:
+        if w.name == w_main.name and args.cu == 0:
+            continue
+        limits = w.cu_limits if cu_ok else (0,)
+        out[w.name] = measure_config(twn, w, args.seed, limits, dev_cus, cpu_seconds=0.3)
+        if not cu_ok and w.cu_limits != (0,):
+            out[w.name]["note"] = "CU-limited runs skipped: this run holds other CU masks"
+    ums, _ = measure_unfused(twn, w_main, main_sets, _steps_for(main_ms * 1e3 * 1.3), 10)
+    out["unfused_pair"] = {"workload": w_main.name, "us_per_step": round(ums * 1e3, 3),
+                           "algorithmic_bytes": w_main.unfused_bytes(),
+                           "gbs_on_unfused_bytes": round(w_main.unfused_bytes() / (ums * 1e-3) / 1e9, 1),
+                           "fused_speedup": round(ums / main_ms, 4)}
+    return out
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -506,7 +615,8 @@ def main(argv=None):
     dev_cus = torch.cuda.get_device_properties(0).multi_processor_count
     call_cus = args.cu if 0 < args.cu < dev_cus else dev_cus
     masked = twn.cu_masked_stream(args.cu) if args.cu > 0 else None
-    ms, wall = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup, stream=masked)
+    ms, wall, dist = measure_fused(twn, w, sets, args.cu, args.steps, args.warmup, stream=masked,
+                                   with_distribution=True)
     bytes_call = w.fused_bytes()
     gbs = bytes_call / (ms * 1e-3) / 1e9
     rows_per_s = w.rows / (ms * 1e-3)
@@ -535,6 +645,7 @@ def main(argv=None):
                                                        w.hidden, w.n, w.rows, call_cus, dev_cus))),
         "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "token_rows_per_s": round(rows_per_s, 1),
+        "per_call_distribution": dist,
         "algorithmic_bytes_per_step": bytes_call,
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
@@ -583,6 +694,9 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(inp, w, _from_dev(d0["out"], w.dtype),
                                               _from_dev(d0["res_out"], w.dtype), args.cpu_seconds)
 
+    if not args.no_per_config:
+        result["per_config"] = measure_per_config(twn, args, w, sets, ms, dev_cus)
+
     if args.report:
         rep = {"main": result, "kernel_source_sha256": kernel_source_hash()}
         ums, _ = measure_unfused(twn, w, sets, max(50, args.steps // 4), 10)
@@ -618,7 +732,6 @@ def main(argv=None):
         ov["overlap_gemm_unmasked_speedup_vs_sequential"] = (ov["sequential_all_cus_us"] /
                                                              ov["overlapped_gemm_unmasked_us"])
         rep["two_split_overlap"] = ov
-        rep["per_call_distribution"] = measure_distribution(twn, w, sets)
         if w.dtype == "bf16" and w.rows >= 64:
             rep["rows_scaling"] = measure_rows_scaling(twn, w, sets[0])
         cms, cbytes = measure_copy(twn, 2 * MALL_BYTES, 200, 20)

@@ -48,3 +48,16 @@ def test_refuses_more_than_one_gpu():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_batch_distribution_percentiles():
+    d = bench.batch_distribution([float(v) for v in range(1, 12)], 3)   # 1..11
+    assert d == {"batches": 11, "calls_per_batch": 3, "median_us": 6.0, "p10_us": 2.0,
+                 "p90_us": 10.0}
+    assert bench.batch_distribution([], 3) is None
+
+
+def test_steps_keep_measurements_near_the_target_time():
+    assert bench._steps_for(30.0) == 666          # 20 ms of 30 us calls
+    assert bench._steps_for(800.0) == 30          # at least 30 steps
+    assert bench._steps_for(1.0) == 2000          # at most 2000 steps
