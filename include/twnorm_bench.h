@@ -47,12 +47,16 @@ tw_status tw_stream_mix(const void* const* srcs, int n_src, void* const* dsts, i
 /*
  * Tuning hook: force the fused kernel's launch shape to `waves` wavefronts
  * per token row with `chunks_per_lane` 16-byte chunks per lane (both 0 =
- * automatic choice), and cap the persistent grid at `wgs_per_cu` workgroups
- * per CU (0 = as many as the CU holds).  Applies to the later calls made
- * from the calling thread only (the setting is per host thread, so one
- * thread's tuning never changes or fails another thread's calls); a shape
- * that cannot cover a row returns TW_ERR_UNSUPPORTED at that thread's call.  Neither the shape nor the grid cap changes any result bit: every
- * shape adds in the same order.  Returns TW_ERR_INVALID_ARG for
+ * automatic choice), and with `wgs_per_cu` > 0 run rows wider than 32
+ * chunks on a persistent grid of at most `wgs_per_cu` workgroups per CU of
+ * the call (0 = the default grid: one workgroup per row on the whole chip, a
+ * persistent grid of as many workgroups as each CU holds on a CU-limited
+ * call).  Applies to the later calls made from the calling thread only (the
+ * setting is per host thread, so one thread's tuning never changes or fails
+ * another thread's calls); a shape that cannot cover a row returns
+ * TW_ERR_UNSUPPORTED at that thread's call.  Neither the shape nor the grid
+ * changes any result bit: every shape adds in the same order.  Returns
+ * TW_ERR_INVALID_ARG for
  * waves outside [0,16], chunks_per_lane not in {0,1,2,3,4,6,8}, only one of
  * the two being 0, or wgs_per_cu < 0.
  */

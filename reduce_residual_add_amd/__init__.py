@@ -415,9 +415,10 @@ def shutdown() -> None:
 
 
 def set_fused_shape(waves: int = 0, chunks_per_lane: int = 0, wgs_per_cu: int = 0) -> None:
-    """Force the fused kernel's launch shape (0, 0 = automatic) and cap its
-    persistent grid at wgs_per_cu workgroups per CU (0 = no cap), for the
-    calling thread's later calls."""
+    """Force the fused kernel's launch shape (0, 0 = automatic) and, with
+    wgs_per_cu > 0, run it on a persistent grid of at most wgs_per_cu
+    workgroups per CU (0 = the default grid), for the calling thread's later
+    calls."""
     _check(load().tw_set_fused_shape(int(waves), int(chunks_per_lane), int(wgs_per_cu)))
 
 

@@ -9,7 +9,8 @@
 //
 //   loads   N partial chunks + 1 residual chunk per 16-byte chunk slot,
 //           all issued before the first add (memory-level parallelism);
-//           the next row's loads are in flight while this row finishes
+//           on a persistent grid the next row's loads are in flight while
+//           this row finishes
 //   sum     s = p_0 + ... + p_{N-1} in index order, x = r + s   (float32)
 //   store   residual_out = round(x)            (the X = X + Y update)
 //   reduce  sum of x^2: per 16-byte chunk -> one DPP / ds_swizzle butterfly
@@ -239,13 +240,15 @@ __device__ __forceinline__ u32x4 scale_chunk(const float* x, float inv, const u3
 
 // ---------------------------------------------------------------------------
 // Wide rows: one workgroup of W wavefronts (blockDim.x = 64 W <= 64 MAXW) per
-// row, each lane owning K chunk slots c = tid + k * blockDim.x.  The grid is
-// persistent (at most the workgroups the chip holds at once) and each
-// workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ...  The loop is
-// software-pipelined: as soon as a row's sums are in registers, the loads of
-// the workgroup's next row are issued, so HBM keeps streaming while the row's
-// sum of squares is reduced, scaled and stored.  Raw chunks of one row sit
-// in K * (N + 1) * 4 VGPRs, the float32 row in K * E.
+// row, each lane owning K chunk slots c = tid + k * blockDim.x.  Each
+// workgroup walks rows blockIdx.x, blockIdx.x + gridDim.x, ...  On the whole
+// chip the grid has one workgroup per row, so each walks a single row; on a
+// CU-limited call the grid is persistent (at most the workgroups those CUs
+// hold at once) and the loop is software-pipelined: as soon as a row's sums
+// are in registers, the loads of the workgroup's next row are issued, so HBM
+// keeps streaming while the row's sum of squares is reduced, scaled and
+// stored.  Raw chunks of one row sit in K * (N + 1) * 4 VGPRs, the float32
+// row in K * E.
 // MAXW sets the launch bound: 4 (256 threads) leaves the compiler up to 512
 // VGPRs per lane, 8 (512 threads) up to 256, 16 (1024 threads) caps it at 128.
 // ---------------------------------------------------------------------------

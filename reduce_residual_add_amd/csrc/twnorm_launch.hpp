@@ -27,8 +27,9 @@ struct Launch {
   int k;           // wide-row kernel: chunk slots per lane; 0 = narrow-row kernel
   int team;        // narrow-row kernel: lanes per row
   int cu_limit;    // 0: whole chip; > 0: persistent grid for that many CUs
-  int device_cus;  // CUs of the device (persistent grid of the wide-row kernel)
-  int wgs_per_cu;  // cap on resident workgroups per CU of that grid (0 = none)
+  int device_cus;  // CUs of the device (persistent whole-chip grid under a cap)
+  int wgs_per_cu;  // > 0: persistent grid of at most this many workgroups per
+                   // CU; 0: no cap (one workgroup per row on the whole chip)
 };
 
 // n in [1, 8] and [9, 16] are instantiated in separate translation units.

@@ -265,7 +265,10 @@ bool shape_spills(tw_dtype dtype, int n, int waves, int k) {
 }
 
 // Shapes measured fastest on MI355X (HBM-resident inputs, shapes swept over
-// waves x chunk slots) for row widths used in practice.
+// waves x chunk slots at 1024 and 4096 rows, one workgroup per row) for row
+// widths used in practice.  Widths not listed, among them 5120 (4 x 3 beats
+// 8 x 2 by 1-3%) and 16384 with few partials (4 x 8 beats 16 x 2 by 2-3%),
+// take the default rule below.
 struct TunedShape {
   int elem_bytes;
   int64_t chunks;
@@ -276,12 +279,10 @@ static const TunedShape kTuned[] = {
     {2, 1024, 5, 16, 4, 4},  // 8192 bf16 features, many partials
     {2, 1024, 1, 3, 8, 2},   // 8192 bf16 features, few partials
     {2, 512, 1, 3, 8, 1},    // 4096 bf16 features, few partials
-    {2, 640, 3, 6, 8, 2},    // 5120 bf16 features
-    {2, 896, 1, 3, 7, 2},    // 7168 bf16 features, few partials (+4% over 4 x 4)
-    {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials (+4% over 4 x 6)
-    {2, 1536, 7, 16, 6, 4},  // 12288 bf16 features, many partials (+2% over 4 x 6)
-    {2, 2048, 1, 3, 16, 2},  // 16384 bf16 features, few partials (+2% over 4 x 8)
-    {2, 2048, 4, 6, 16, 2},  // 16384 bf16 features, 4-6 partials (+5% over 4 x 8)
+    {2, 896, 1, 3, 7, 2},    // 7168 bf16 features, few partials (+4% over 4 x 4 at 1024 rows)
+    {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials
+    {2, 1536, 7, 16, 6, 4},  // 12288 bf16 features, many partials (+4% over 4 x 6)
+    {2, 2048, 4, 6, 16, 2},  // 16384 bf16 features, 4-6 partials (+2-4% over 4 x 8)
 };
 
 // Shapes measured fastest when a call runs on at most half of the CUs: on 8,

@@ -48,9 +48,10 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
 // (from the build's register-fit table).
 bool shape_spills(tw_dtype dtype, int n, int waves, int k);
 
-// Force (waves, k) for wide rows ((0, 0) restores the automatic choice) and
-// cap the persistent grid at wgs_per_cu workgroups per CU (0 = no cap), for
-// the calling thread's later calls.
+// Force (waves, k) for wide rows ((0, 0) restores the automatic choice) and,
+// with wgs_per_cu > 0, run the wide-row kernel on a persistent grid of at
+// most wgs_per_cu workgroups per CU (0 = the default grid), for the calling
+// thread's later calls.
 tw_status set_override(int waves, int k, int wgs_per_cu);
 int wgs_per_cu_cap();
 

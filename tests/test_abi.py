@@ -250,7 +250,8 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 16384, 4) == (16, 2, 0)
     assert twn.query_fused_shape(BF16, 16384, 8) == (4, 8, 0)
     assert twn.query_fused_shape(BF16, 4096, 2) == (8, 1, 0)
-    assert twn.query_fused_shape(BF16, 5120, 4) == (8, 2, 0)
+    assert twn.query_fused_shape(BF16, 5120, 4) == (4, 3, 0)     # default rule: 4 waves
+    assert twn.query_fused_shape(BF16, 16384, 2) == (4, 8, 0)
     assert twn.query_fused_shape(BF16, 2048, 2) == (4, 1, 0)     # 4 waves, fewest slots
     w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
