@@ -61,10 +61,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
+def counter_traffic(workload: str, cu: int = 0):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, or None if absent or taken on a different kernel source."""
-    path = os.path.join(PROFILE_DIR, f"fused_{workload}_counters.md")
+    this workload (at n_cu_limit `cu`, 0 = whole chip), or None if absent or
+    taken on a different kernel source."""
+    tag = f"_cu{cu}" if cu > 0 else ""
+    path = os.path.join(PROFILE_DIR, f"fused_{workload}{tag}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -547,7 +549,8 @@ def measure_config(twn, w, seed, cu_limits, dev_cus, cpu_seconds):
              "token_rows_per_s": round(w.rows / (ms * 1e-3), 1), "steps": steps,
              "rotating_sets": n_sets, "per_call_distribution": dist,
              "launch_shape": list(twn.query_fused_shape(code, w.hidden, w.n, w.rows, call_cus,
-                                                        dev_cus))}
+                                                        dev_cus)),
+             "traffic_per_call": counter_traffic(w.name, cu if call_cus < dev_cus else 0)}
         torch.cuda.synchronize()
         d0 = sets[0]
         # the timed calls ended on the last set; set 0 holds the outputs of
@@ -649,7 +652,8 @@ def main(argv=None):
         "algorithmic_bytes_per_step": bytes_call,
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_GBS, 4), "traffic": counter_traffic(w.name)},
+                     "frac": round(gbs / PEAK_GBS, 4),
+                     "traffic": counter_traffic(w.name, args.cu if call_cus < dev_cus else 0)},
     }
     if args.cu > 0:
         # the same calls issued from the default stream: each one pays the
