@@ -163,7 +163,8 @@ def assert_parity(got_storage, ref, dtype, what="", bound=None):
         raise ValueError("bf16 parity needs the per-element float32 error bound")
     rep = tolerance_report(got_storage, ref, dtype, bound)
     if os.environ.get("TW_PRINT_EXACT"):
-        print(f"EXACT {what} {rep.get('exact_frac')} n={rep.get('n')}", flush=True)
+        print(f"EXACT {what} {rep.get('exact_frac')} n={rep.get('n')} "
+              f"exempt={rep.get('ulp_exempt')} max_ulp_all={rep.get('max_ulp_all')}", flush=True)
     assert rep["fails"] == 0, f"{what}: {rep}"
     if dtype == "bf16":
         assert rep["max_ulp"] <= 1, f"{what}: more than one bf16 ulp from the oracle: {rep}"

@@ -375,14 +375,21 @@ def test_allgather_store_leaves_other_rows(twn):
 
 
 def test_many_rows_per_workgroup(twn):
-    """Rows far beyond the resident grid: every workgroup walks tens of rows
-    through the software-pipelined loop (and the narrow-row kernel loops too).
-    Every row is checked against the oracle."""
+    """Rows far beyond the resident grid.  On the whole chip every row gets a
+    workgroup of its own; on 8 CUs, and under a cap of one workgroup per CU,
+    the grid is persistent and every workgroup walks tens to thousands of rows
+    through the software-pipelined loop (the narrow-row kernel loops too).
+    Every row of every run is checked against the oracle."""
     for n, rows, hidden, dtype in [(3, 20011, 1024, "bf16"), (2, 40000, 64, "f32")]:
-        _say(f"[many rows] n={n} rows={rows} H={hidden} {dtype}")
         inp = workloads.make_random(n, rows, hidden, dtype, seed=rows)
-        out, res_out = _run_fused(twn, inp)
-        _assert_all_rows(inp, out, res_out, f"many rows n={n}", chunk=4096)
+        for cu, cap in ((0, 0), (8, 0), (0, 1)):
+            _say(f"[many rows] n={n} rows={rows} H={hidden} {dtype} n_cu_limit={cu} cap={cap}")
+            twn.set_fused_shape(0, 0, cap)
+            try:
+                out, res_out = _run_fused(twn, inp, n_cu_limit=cu)
+            finally:
+                twn.set_fused_shape(0, 0, 0)
+            _assert_all_rows(inp, out, res_out, f"many rows n={n} cu{cu} cap{cap}", chunk=4096)
 
 
 def test_same_partial_twice(twn):
@@ -780,8 +787,9 @@ def test_stream_copy_copies_bytes(twn, nbytes, cu):
 
 
 def test_grid_cap_changes_no_bit(twn):
-    """Capping the persistent grid (1 or 2 workgroups per CU, so each
-    workgroup walks more rows) changes no result bit."""
+    """A persistent whole-chip grid capped at 1 or 2 workgroups per CU (each
+    workgroup walks several rows through the pipelined loop) gives the same
+    bits as the default grid of one workgroup per row."""
     import torch
     _say("[grid cap] 1 and 2 workgroups per CU")
     inp = workloads.make_random(8, 700, 8192, "bf16", seed=31)
