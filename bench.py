@@ -152,25 +152,32 @@ def n_rotating_sets(set_bytes, requested):
 
 def time_batches(step_fns, est_us_per_call, stream=None, batches=30, batch_ms=1.0):
     """Per-call time distribution over `batches` batches of back-to-back
-    calls, each batch a whole number of passes over the rotating sets and
-    about `batch_ms` of GPU time, with one event between consecutive batches.
+    calls, each batch about `batch_ms` of GPU time and a whole number of
+    passes over the rotating sets (or, with more sets than four batches
+    hold, consecutive calls of the rotation), with one event between
+    consecutive batches.
     An event recorded between two kernels on MI355X costs about 1 us of GPU
     time (measured: 30.3 -> 31.4 us per call with an event every 3 calls), so
     the headline mean is timed without them and this pass runs after it, with
     batches long enough that the events cost about 0.1%."""
     import torch
     n = len(step_fns)
-    passes = max(1, int(round(batch_ms * 1e3 / max(est_us_per_call, 1e-3) / n)))
-    calls = passes * n
+    want = max(1, int(round(batch_ms * 1e3 / max(est_us_per_call, 1e-3))))
+    # whole passes over the sets, unless one pass alone is far longer than a
+    # batch (thousands of sets of a latency-bound workload): then each batch
+    # continues the rotation where the previous one stopped
+    calls = max(1, int(round(want / n))) * n if n <= 4 * want else want
     for f in step_fns:
         f()
     torch.cuda.synchronize()
     s = stream if stream is not None else torch.cuda.current_stream()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
     marks[0].record(s)
+    k = 0
     for b in range(batches):
-        for i in range(calls):
-            step_fns[i % n]()
+        for _ in range(calls):
+            step_fns[k % n]()
+            k += 1
         marks[b + 1].record(s)
     torch.cuda.synchronize()
     per_call = [marks[b].elapsed_time(marks[b + 1]) * 1e3 / calls for b in range(batches)]
