@@ -5,7 +5,8 @@ One token split's fused calls run on the library's stream limited to the
 first k CUs while the other split's row-parallel GEMM (the MLP down-
 projection of an 8-way tensor-parallel 70B-class layer, [1024, 3584] x
 [3584, 8192] bf16, torch / hipBLASLt) runs beside them, first unmasked on an
-ordinary stream, then on the k-complement stream ("TokenWeave: Efficient
+ordinary stream, then on the k-complement stream; last, whole-chip fused
+calls on an ordinary stream beside the unmasked GEMM ("TokenWeave: Efficient
 Compute-Communication Overlap for Distributed LLM Inference", the split into
 two token blocks, one computing while the other communicates).  Each fused
 call writes its own outputs; all of them must match the oracle, and every
@@ -40,8 +41,11 @@ def main(k: int) -> int:
     masked = twn.cu_masked_stream(k)
     comp = twn.cu_complement_stream(k)
     side = torch.cuda.Stream()
+    side2 = torch.cuda.Stream()
     calls = 4
-    for gemm_stream, label in ((side, "GEMM unmasked"), (comp, "GEMM on the complement")):
+    for gemm_stream, fused_stream, cu, label in (
+            (side, masked, k, "GEMM unmasked"), (comp, masked, k, "GEMM on the complement"),
+            (side, side2, 0, "GEMM unmasked beside whole-chip fused calls")):
         print(f"[overlap child] {label}", flush=True)
         outs = [(torch.full_like(res, 7.0), torch.full_like(res, 7.0)) for _ in range(calls)]
         cs = [torch.empty_like(solo_c) for _ in range(calls)]
@@ -49,10 +53,10 @@ def main(k: int) -> int:
         with torch.cuda.stream(gemm_stream):
             for c in cs:
                 torch.matmul(a, b, out=c)
-        with torch.cuda.stream(masked):
+        with torch.cuda.stream(fused_stream):
             for o, r in outs:
                 twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=o, residual_out=r,
-                                         n_cu_limit=k)
+                                         n_cu_limit=cu)
         torch.cuda.synchronize()
         for i, (o, r) in enumerate(outs):
             assert_parity(from_dev(r, "bf16"), ref_res, "bf16", f"{label} call {i} residual_out",
