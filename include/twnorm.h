@@ -55,6 +55,9 @@
  *              k in [1, CUs) runs the kernel on at most k CUs (persistent grid
  *              on a cached CU-masked stream, ordered after and before `stream`
  *              by events).  Results are bit-identical for every n_cu_limit.
+ *              Such calls launch workgroups of at most 10 wavefronts, so rows
+ *              wider than 40960 bf16 (20480 fp32) features return
+ *              TW_ERR_UNSUPPORTED with a CU limit.
  *              Each distinct CU mask needs a hardware queue of its own until
  *              tw_shutdown(): at most 3 distinct masks (limits k, and
  *              complements from tw_cu_complement_stream) per device and

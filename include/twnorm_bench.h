@@ -54,8 +54,11 @@ tw_status tw_stream_mix(const void* const* srcs, int n_src, void* const* dsts, i
  * call).  Applies to the later calls made from the calling thread only (the
  * setting is per host thread, so one thread's tuning never changes or fails
  * another thread's calls); a shape that cannot cover a row returns
- * TW_ERR_UNSUPPORTED at that thread's call.  Neither the shape nor the grid
- * changes any result bit: every shape adds in the same order.  Returns
+ * TW_ERR_UNSUPPORTED at that thread's call, and so does a shape of more than
+ * 10 wavefronts at a CU-limited call.  A forced shape also applies to rows of
+ * at most 32 chunks, which otherwise take the narrow-row kernel.  Neither the
+ * shape nor the grid changes any result bit: every shape adds in the same
+ * order.  Returns
  * TW_ERR_INVALID_ARG for
  * waves outside [0,16], chunks_per_lane not in {0,1,2,3,4,6,8}, only one of
  * the two being 0, or wgs_per_cu < 0.

@@ -304,10 +304,10 @@ static const TunedShape kTunedLimited[] = {
 //    among the spill-free (W, K) the fewest idle chunk slots (ties: smaller
 //    K); if every candidate spills, the fewest idle slots regardless.
 static tw_status throughput_shape(tw_dtype dtype, int b, int64_t chunks, int64_t hidden, int n,
-                                  Shape* shape) {
+                                  int max_waves, Shape* shape) {
   for (const TunedShape& t : kTuned) {
     if (t.elem_bytes == b && t.chunks == chunks && n >= t.n_lo && n <= t.n_hi &&
-        !shape_spills(dtype, n, t.waves, t.k)) {
+        t.waves <= max_waves && !shape_spills(dtype, n, t.waves, t.k)) {
       *shape = Shape{t.waves, t.k, 0};
       return TW_OK;
     }
@@ -325,7 +325,7 @@ static tw_status throughput_shape(tw_dtype dtype, int b, int64_t chunks, int64_t
   int64_t best_waste = -1, any_waste = -1;
   for (int k : kAllowedK) {
     const int64_t w = (chunks + 64 * k - 1) / (64 * k);
-    if (w > 16) continue;
+    if (w > max_waves) continue;
     const int64_t waste = w * 64 * k - chunks;
     if (any_waste < 0 || waste < any_waste) {
       any_waste = waste;
@@ -338,31 +338,50 @@ static tw_status throughput_shape(tw_dtype dtype, int b, int64_t chunks, int64_t
       best_k = k;
     }
   }
-  if (any_waste < 0) return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide", (long long)hidden);
+  if (any_waste < 0)
+    return fail(TW_ERR_UNSUPPORTED, "hidden %lld too wide for workgroups of at most %d wavefronts",
+                (long long)hidden, max_waves);
   *shape = best_waste >= 0 ? Shape{best_w, best_k, 0} : Shape{any_w, any_k, 0};
   return TW_OK;
 }
+
+// Widest workgroup, in wavefronts, that a CU-limited call launches: 640
+// threads (the 10 x 1 shape measured on CU-masked queues).  Workgroups of 16
+// wavefronts have not been run on a CU-masked queue here (an exploratory probe
+// of 1024-thread workgroups on one stalled, cause not established), so
+// CU-limited calls never launch them.
+constexpr int kMaxLimitedWaves = 10;
 
 // Automatic shape.  The results do not depend on it (the order of every
 // addition is fixed by the row width), so it may follow the call:
 //  * rows of at most 32 chunks: narrow-row kernel, smallest power-of-two team;
 //  * fewer rows than CUs (decode-sized calls, one workgroup per row, most CUs
-//    idle): as many wavefronts as the row fills (at most 16) with the fewest
-//    chunk slots per lane, so each lane issues the fewest loads in a row, if
-//    that spills nothing;
+//    idle): as many wavefronts as the row fills (at most 16, or
+//    kMaxLimitedWaves on a CU-limited call) with the fewest chunk slots per
+//    lane, so each lane issues the fewest loads in a row, if that spills
+//    nothing;
 //  * else the whole-chip shape above, or, when the call runs on at most half
 //    of the device's CUs, a shape measured for that regime if there is one.
+// A CU-limited call never uses more than kMaxLimitedWaves wavefronts per
+// workgroup, so rows wider than kMaxLimitedWaves x 64 x 8 chunks (40960 bf16)
+// return TW_ERR_UNSUPPORTED there.
 tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int cus, int device_cus,
                        Shape* shape) {
   const int b = elem_bytes(dtype);
   if (b == 0) return fail(TW_ERR_INVALID_ARG, "unknown dtype");
   if (n < 1 || n > TW_MAX_PARTIALS) return fail(TW_ERR_INVALID_ARG, "n out of range");
   const int64_t chunks = hidden * b / 16;
+  const bool limited = cus < device_cus;
+  const int max_waves = limited ? kMaxLimitedWaves : 16;
   const int ow = g_override_waves, ok = g_override_k;
   if (ow > 0 && ok > 0) {
     if ((int64_t)ow * 64 * ok < chunks)
       return fail(TW_ERR_UNSUPPORTED, "forced shape %d waves x %d chunks cannot cover %lld chunks",
                   ow, ok, (long long)chunks);
+    if (ow > max_waves)
+      return fail(TW_ERR_UNSUPPORTED,
+                  "forced shape of %d waves exceeds the %d-wavefront workgroups of CU-limited calls",
+                  ow, max_waves);
     *shape = Shape{ow, ok, 0};
     return TW_OK;
   }
@@ -373,7 +392,7 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
     return TW_OK;
   }
   if (rows < cus) {
-    const int64_t w = std::min<int64_t>(16, (chunks + 63) / 64);
+    const int64_t w = std::min<int64_t>(max_waves, (chunks + 63) / 64);
     for (int k : kAllowedK) {
       if (w * 64 * k >= chunks) {
         if (!shape_spills(dtype, n, (int)w, k)) {
@@ -385,14 +404,14 @@ tw_status choose_shape(tw_dtype dtype, int64_t hidden, int n, int64_t rows, int 
     }
   }
   Shape t{};
-  tw_status st = throughput_shape(dtype, b, chunks, hidden, n, &t);
+  tw_status st = throughput_shape(dtype, b, chunks, hidden, n, max_waves, &t);
   if (st != TW_OK) return st;
   // On at most half of the device's CUs a call is bound by what each CU
   // issues and keeps in flight, not by HBM, and other shapes win there.
   if (2 * (int64_t)cus <= device_cus) {
     for (const TunedShape& u : kTunedLimited) {
       if (u.elem_bytes == b && u.chunks == chunks && n >= u.n_lo && n <= u.n_hi &&
-          !shape_spills(dtype, n, u.waves, u.k)) {
+          u.waves <= max_waves && !shape_spills(dtype, n, u.waves, u.k)) {
         t = Shape{u.waves, u.k, 0};
         break;
       }

@@ -273,6 +273,17 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 4096, 2, rows=8, cus=256) == (8, 1, 0)
     assert twn.query_fused_shape(BF16, 16384, 2, rows=8, cus=256) == (16, 2, 0)
     assert twn.query_fused_shape(F32, 64, 2, rows=1, cus=256) == (0, 0, 16)   # still a team
+    # CU-limited calls launch workgroups of at most 10 wavefronts
+    assert twn.query_fused_shape(BF16, 8192, 8, rows=4, cus=8) == (10, 2, 0)
+    assert twn.query_fused_shape(BF16, 5120, 4, rows=5, cus=16) == (10, 1, 0)
+    assert twn.query_fused_shape(BF16, 16384, 5, rows=4096, cus=8) == (4, 8, 0)
+    assert twn.query_fused_shape(BF16, 16384, 5, rows=4096, cus=256) == (16, 2, 0)
+    assert twn.query_fused_shape(BF16, 40960, 2, rows=4, cus=8) == (10, 8, 0)
+    with pytest.raises(twn.TwError, match="10 wavefronts"):
+        twn.query_fused_shape(BF16, 40968, 2, rows=4, cus=8)
+    with pytest.raises(twn.TwError):
+        twn.query_fused_shape(F32, 20484, 2, rows=4, cus=8)
+    assert twn.query_fused_shape(F32, 20480, 2, rows=4, cus=8) == (10, 8, 0)
     with pytest.raises(twn.TwError):
         twn.query_fused_shape(BF16, 8192, 8, rows=-1)
     with pytest.raises(twn.TwError):
@@ -289,6 +300,15 @@ def test_shape_choice(lib):
         assert twn.query_fused_shape(BF16, 8192, 8) == (8, 2, 0)
         with pytest.raises(twn.TwError):
             twn.query_fused_shape(BF16, 16384, 8)   # 8 x 64 x 2 < 2048 chunks
+    finally:
+        twn.set_fused_shape(0, 0)
+    twn.set_fused_shape(16, 1)
+    try:
+        assert twn.query_fused_shape(BF16, 8192, 8, rows=4096, cus=256) == (16, 1, 0)
+        with pytest.raises(twn.TwError, match="CU-limited"):
+            twn.query_fused_shape(BF16, 8192, 8, rows=4096, cus=8)   # more than 10 wavefronts
+        with pytest.raises(twn.TwError, match="CU-limited"):
+            twn.query_fused_shape(BF16, 256, 8, rows=4, cus=8)     # narrow rows too
     finally:
         twn.set_fused_shape(0, 0)
     for bad in [(17, 1), (4, 5), (0, 2), (2, 0), (-1, 1), (4, 4, -1)]:

@@ -403,6 +403,37 @@ def test_many_rows_per_workgroup(twn):
             _assert_all_rows(inp, out, res_out, f"many rows n={n} cu{cu} cap{cap}", chunk=4096)
 
 
+def test_decode_rows_on_cu_limits(twn):
+    """Decode-sized calls (fewer rows than the CU limit) on 8 and 16 CUs: one
+    workgroup of at most 10 wavefronts per row.  Every row against the oracle,
+    and bit-identical to the whole-chip call, which uses 16 wavefronts."""
+    cases = [(8, 1, 8192, 8), (8, 7, 8192, 8), (4, 5, 5120, 16), (2, 3, 4096, 8),
+             (2, 15, 16384, 16), (3, 2, 40960, 8)]
+    for i, (n, rows, hidden, cu) in enumerate(cases):
+        _say(f"[decode on CUs] n={n} rows={rows} H={hidden} n_cu_limit={cu}")
+        inp = workloads.make_random(n, rows, hidden, "bf16", seed=500 + i)
+        out_cu, res_cu = _run_fused(twn, inp, n_cu_limit=cu)
+        _assert_rows(inp, out_cu, res_cu, f"decode rows={rows} H={hidden} cu{cu}")
+        out0, res0 = _run_fused(twn, inp)
+        assert np.array_equal(out_cu, out0) and np.array_equal(res_cu, res0)
+
+
+def test_cu_limited_call_refuses_rows_past_its_workgroups(twn):
+    """A CU-limited call on rows wider than 10 wavefronts can cover returns
+    TW_ERR_UNSUPPORTED and writes nothing; the whole-chip call takes them."""
+    import torch
+    _say("[cu limit] 65536-wide rows refused on 8 CUs")
+    inp = workloads.make_random(2, 3, 65536, "bf16", seed=17)
+    parts, res, wt = inputs_to_dev(inp)
+    out = torch.full_like(res, 7.0)
+    res_out = torch.full_like(res, 7.0)
+    with pytest.raises(twn.TwError, match="10 wavefronts"):
+        twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=out, residual_out=res_out,
+                                 n_cu_limit=8)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((res_out == 7.0).all())
+
+
 def test_same_partial_twice(twn):
     """Passing one buffer twice sums it twice (reads may repeat)."""
     import torch
