@@ -550,6 +550,29 @@ def test_every_partial_count(twn, n):
         _assert_rows(inp, out, res_out, f"n={n} H={hidden} {dtype}")
 
 
+@pytest.mark.parametrize("n", list(range(1, 17)))
+def test_reduce_every_partial_count(twn, n):
+    """tw_reduce, the unfused path's first kernel, is instantiated per partial
+    count and format: every one against the oracle's stored sum, on totals
+    that end inside a block (5 x 1000 bf16, 3 x 1540 fp32), with the output
+    written over the first partial in the last case (an exact alias the ABI
+    allows)."""
+    import torch
+    _say(f"[reduce every n] n={n}")
+    for rows, hidden, dtype, in_place in [(5, 1000, "bf16", False), (3, 1540, "f32", False),
+                                          (4, 2056, "bf16", True)]:
+        inp = workloads.make_random(n, rows, hidden, dtype, seed=300 * n + hidden)
+        parts, _, _ = inputs_to_dev(inp)
+        red = twn.reduce(parts, out=parts[0] if in_place else None)
+        torch.cuda.synchronize()
+        if in_place:
+            assert red.data_ptr() == parts[0].data_ptr()
+        ref = O.reduce_from_storage(inp)
+        mag = sum(np.abs(O.decode(p, dtype)) for p in inp["partials"])
+        bound = (n + 1) * 2.0 ** -24 * mag if dtype == "bf16" else None
+        assert_parity(from_dev(red, dtype), ref, dtype, f"reduce n={n} H={hidden} {dtype}", bound)
+
+
 # ---------------------------------------------------------------------------
 # Traffic-pattern measurement aid (not part of the method): every destination
 # word is the wrap-around uint32 sum of the source words; bytes past the end
