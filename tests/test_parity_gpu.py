@@ -385,6 +385,41 @@ def test_allgather_store_leaves_other_rows(twn):
         assert np.all(untouched == O.bf16_encode_rne(np.array([-2.0]))[0])
 
 
+AG_CASES = [
+    # (n partials, rows, hidden, dtype, gather buffers, row offset, total rows, n_cu_limit)
+    (2, 9, 4096, "bf16", 1, 0, 9, 0),          # one buffer: the plain fused call's store
+    (5, 11, 8200, "bf16", 16, 13, 40, 0),      # the most gather buffers, ragged row
+    (3, 37, 200, "bf16", 16, 3, 64, 0),        # narrow rows: the team kernel stores 16 times
+    (4, 6, 3000, "f32", 5, 2, 8, 0),           # fp32
+    (8, 300, 8192, "bf16", 8, 100, 2400, 8),   # on 8 CUs (persistent grid)
+]
+
+
+@pytest.mark.parametrize("case", AG_CASES, ids=lambda c: f"n{c[0]}-r{c[1]}-h{c[2]}-{c[3]}-ag{c[4]}-cu{c[7]}")
+def test_allgather_store_shapes(twn, case):
+    """The AllGather store across its shapes: 1-16 gather buffers, the wide-
+    and narrow-row kernels, fp32, a CU limit.  Every gather buffer holds the
+    normalised rows at the offset, against the oracle, and nothing else."""
+    import torch
+    n, rows, hidden, dtype, n_ag, off, total, cu = case
+    _say(f"[allgather shapes] n={n} rows={rows} H={hidden} {dtype} buffers={n_ag} offset={off} cu={cu}")
+    inp = workloads.make_random(n, rows, hidden, dtype, seed=700 + n_ag + hidden)
+    parts, res, wt = inputs_to_dev(inp)
+    tdt = res.dtype
+    gathers = [torch.full((total, hidden), -2.0, dtype=tdt, device="cuda") for _ in range(n_ag)]
+    res_out = twn.fused_reduce_rmsnorm_allgather(parts, res, wt, inp["eps"], gathers, off,
+                                                 n_cu_limit=cu)
+    torch.cuda.synchronize()
+    ref_out, ref_res, b_out, b_res = reference(inp)
+    assert_parity(from_dev(res_out, dtype), ref_res, dtype, "residual_out", b_res)
+    minus2 = O.encode(np.array([-2.0]), dtype)[0]
+    for j, g in enumerate(gathers):
+        gh = from_dev(g, dtype)
+        assert_parity(gh[off:off + rows], ref_out, dtype, f"gather buffer {j}", b_out)
+        rest = np.concatenate([gh[:off], gh[off + rows:]])
+        assert np.all(rest == minus2), f"gather buffer {j}: rows outside the shard were written"
+
+
 def test_many_rows_per_workgroup(twn):
     """Rows far beyond the resident grid.  On the whole chip every row gets a
     workgroup of its own; on 8 CUs, and under a cap of one workgroup per CU,
