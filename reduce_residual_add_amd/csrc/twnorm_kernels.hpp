@@ -281,10 +281,11 @@ template <class D, int N, int K, int MAXW>
 struct RowPlan {
   static constexpr int kTarget = MAXW <= 8 ? 256 : 128;
   static constexpr int kFixed = K * D::kElems + K * 4 + 48;
-  static constexpr int kWhole = (N + 1) * K * 4;
+  static constexpr bool kWholeRow = (N + 1) * K * 4 + kFixed <= kTarget;
   static constexpr int kFit = (kTarget - kFixed) / (K * 4);
-  static constexpr int kGroup =
-      kWhole + kFixed <= kTarget ? N : (kFit < 1 ? 1 : (kFit < N ? kFit : N));
+  // partials per group when the whole row does not fit (may be all N: the
+  // residual then still waits until they are summed)
+  static constexpr int kGroup = kWholeRow ? N : (kFit < 1 ? 1 : (kFit < N ? kFit : N));
 };
 
 // `residual` carries no __restrict__: the in-place update passes the same
@@ -297,6 +298,7 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict
                   int64_t rows, int chunks, float hidden_f, float eps) {
   constexpr int E = D::kElems;
   constexpr int G = RowPlan<D, N, K, MAXW>::kGroup;
+  constexpr bool kWholeRow = RowPlan<D, N, K, MAXW>::kWholeRow;
   __shared__ float red[2][MAXW * K];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -355,7 +357,7 @@ fused_rows_kernel(PartialPtrs pp, const u32x4* residual, const u32x4* __restrict
   // Slots past the row's end load zeros, so they add nothing to the sums,
   // and their stores fall outside the descriptor's range and are dropped.
   const int64_t first = blockIdx.x, stride = gridDim.x, end = rows;
-  if constexpr (G == N) {
+  if constexpr (kWholeRow) {
     // Whole rows: the residual and all N partials of the row in flight at
     // once, and the next row's loads issued as soon as this row's sums are
     // in registers.

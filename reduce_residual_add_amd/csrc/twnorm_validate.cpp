@@ -264,11 +264,13 @@ bool shape_spills(tw_dtype dtype, int n, int waves, int k) {
   return ((kFitMask[dt][n][bucket_of(waves)] >> ki) & 1) == 0;
 }
 
-// Shapes measured fastest on MI355X (HBM-resident inputs, shapes swept over
-// waves x chunk slots at 1024 and 4096 rows, one workgroup per row) for row
-// widths used in practice.  Widths not listed, among them 5120 (4 x 3 beats
-// 8 x 2 by 1-3%) and 16384 with few partials (4 x 8 beats 16 x 2 by 2-3%),
-// take the default rule below.
+// Shapes measured fastest on MI355X (HBM-resident inputs, every K with its
+// fewest covering waves timed at 1024 and 4096 rows, one workgroup per row,
+// partials loaded in groups where a whole row exceeds the register target)
+// for row widths used in practice.  Widths and partial counts not listed take
+// the default rule below, which won the rest of the sweep (for example 4 x 6
+// on 12288-wide rows with 4-16 partials and 4 x 8 on 16384-wide rows with
+// 4-16 partials).
 struct TunedShape {
   int elem_bytes;
   int64_t chunks;
@@ -278,11 +280,13 @@ struct TunedShape {
 static const TunedShape kTuned[] = {
     {2, 1024, 5, 16, 4, 4},  // 8192 bf16 features, many partials
     {2, 1024, 1, 3, 8, 2},   // 8192 bf16 features, few partials
-    {2, 512, 1, 3, 8, 1},    // 4096 bf16 features, few partials
+    {2, 512, 1, 2, 1, 8},    // 4096 bf16, 1-2 partials: one wave per row, no barrier (+3%)
+    {2, 512, 3, 5, 8, 1},    // 4096 bf16, 3-5 partials (+1-6% over 4 x 2 and 1 x 8)
+    {2, 512, 6, 16, 1, 8},   // 4096 bf16, 6-16 partials (+8-11% over 4 x 2)
     {2, 896, 1, 3, 7, 2},    // 7168 bf16 features, few partials (+4% over 4 x 4 at 1024 rows)
     {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials
-    {2, 1536, 7, 16, 6, 4},  // 12288 bf16 features, many partials (+4% over 4 x 6)
-    {2, 2048, 4, 6, 16, 2},  // 16384 bf16 features, 4-6 partials (+2-4% over 4 x 8)
+    {2, 2048, 1, 1, 16, 2},  // 16384 bf16 features, one partial (+10% over 4 x 8)
+    {2, 2048, 2, 2, 8, 4},   // 16384 bf16 features, two partials (+4% over 4 x 8)
 };
 
 // Shapes measured fastest when a call runs on at most half of the CUs: on 8,

@@ -247,11 +247,15 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 8192, 2) == (8, 2, 0)
     assert twn.query_fused_shape(BF16, 8192, 4) == (4, 4, 0)
     assert twn.query_fused_shape(BF16, 7168, 2) == (7, 2, 0)
-    assert twn.query_fused_shape(BF16, 16384, 4) == (16, 2, 0)
+    assert twn.query_fused_shape(BF16, 16384, 4) == (4, 8, 0)
+    assert twn.query_fused_shape(BF16, 16384, 1) == (16, 2, 0)
+    assert twn.query_fused_shape(BF16, 16384, 2) == (8, 4, 0)
     assert twn.query_fused_shape(BF16, 16384, 8) == (4, 8, 0)
-    assert twn.query_fused_shape(BF16, 4096, 2) == (8, 1, 0)
+    assert twn.query_fused_shape(BF16, 4096, 2) == (1, 8, 0)     # one wave per row
+    assert twn.query_fused_shape(BF16, 4096, 4) == (8, 1, 0)
+    assert twn.query_fused_shape(BF16, 4096, 8) == (1, 8, 0)
+    assert twn.query_fused_shape(BF16, 12288, 8) == (4, 6, 0)
     assert twn.query_fused_shape(BF16, 5120, 4) == (4, 3, 0)     # default rule: 4 waves
-    assert twn.query_fused_shape(BF16, 16384, 2) == (4, 8, 0)
     assert twn.query_fused_shape(BF16, 2048, 2) == (4, 1, 0)     # 4 waves, fewest slots
     w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
@@ -277,7 +281,7 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 8192, 8, rows=4, cus=8) == (10, 2, 0)
     assert twn.query_fused_shape(BF16, 5120, 4, rows=5, cus=16) == (10, 1, 0)
     assert twn.query_fused_shape(BF16, 16384, 5, rows=4096, cus=8) == (4, 8, 0)
-    assert twn.query_fused_shape(BF16, 16384, 5, rows=4096, cus=256) == (16, 2, 0)
+    assert twn.query_fused_shape(BF16, 16384, 5, rows=4096, cus=256) == (4, 8, 0)
     assert twn.query_fused_shape(BF16, 40960, 2, rows=4, cus=8) == (10, 8, 0)
     with pytest.raises(twn.TwError, match="10 wavefronts"):
         twn.query_fused_shape(BF16, 40968, 2, rows=4, cus=8)
