@@ -350,10 +350,11 @@ static tw_status throughput_shape(tw_dtype dtype, int b, int64_t chunks, int64_t
 }
 
 // Widest workgroup, in wavefronts, that a CU-limited call launches: 640
-// threads (the 10 x 1 shape measured on CU-masked queues).  Workgroups of 16
-// wavefronts have not been run on a CU-masked queue here (an exploratory probe
-// of 1024-thread workgroups on one stalled, cause not established), so
-// CU-limited calls never launch them.
+// threads, the widest shape the GPU tests run on CU-masked queues.  An
+// exploratory probe that ran 1024-thread workgroups (with register loads and
+// with direct-to-LDS loads) on an 8-CU mask stalled, cause not established;
+// 1024-thread workgroups had run on a 32-CU mask before.  Until the cause is
+// known, CU-limited calls stay on the tested sizes.
 constexpr int kMaxLimitedWaves = 10;
 
 // Automatic shape.  The results do not depend on it (the order of every
