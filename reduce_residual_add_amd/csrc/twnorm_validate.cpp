@@ -283,6 +283,7 @@ static const TunedShape kTuned[] = {
     {2, 512, 1, 2, 1, 8},    // 4096 bf16, 1-2 partials: one wave per row, no barrier (+3%)
     {2, 512, 3, 5, 8, 1},    // 4096 bf16, 3-5 partials (+1-6% over 4 x 2 and 1 x 8)
     {2, 512, 6, 16, 1, 8},   // 4096 bf16, 6-16 partials (+8-11% over 4 x 2)
+    {2, 640, 1, 2, 5, 2},    // 5120 bf16 features, 1-2 partials: every lane busy (+4% over 4 x 3)
     {2, 896, 1, 3, 7, 2},    // 7168 bf16 features, few partials (+4% over 4 x 4 at 1024 rows)
     {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials
     {2, 2048, 1, 1, 16, 2},  // 16384 bf16 features, one partial (+10% over 4 x 8)

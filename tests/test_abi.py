@@ -256,6 +256,7 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 4096, 8) == (1, 8, 0)
     assert twn.query_fused_shape(BF16, 12288, 8) == (4, 6, 0)
     assert twn.query_fused_shape(BF16, 5120, 4) == (4, 3, 0)     # default rule: 4 waves
+    assert twn.query_fused_shape(BF16, 5120, 2) == (5, 2, 0)
     assert twn.query_fused_shape(BF16, 2048, 2) == (4, 1, 0)     # 4 waves, fewest slots
     w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
