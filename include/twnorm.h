@@ -57,7 +57,10 @@
  *              by events).  Results are bit-identical for every n_cu_limit.
  *              Such calls launch workgroups of at most 10 wavefronts, so rows
  *              wider than 40960 bf16 (20480 fp32) features return
- *              TW_ERR_UNSUPPORTED with a CU limit.
+ *              TW_ERR_UNSUPPORTED with a CU limit.  Under HIP-graph capture
+ *              a CU-limited call is captured with its event join and replays
+ *              with the same results, but a graph node carries no CU mask:
+ *              in replay its grid (sized for k CUs) is not confined to them.
  *              Each distinct CU mask needs a hardware queue of its own until
  *              tw_shutdown(): at most 3 distinct masks (limits k, and
  *              complements from tw_cu_complement_stream) per device and

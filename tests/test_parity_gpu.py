@@ -574,6 +574,38 @@ def test_graph_capture_replays(twn):
         assert torch.equal(red, eager_red) and torch.equal(out2, eager_out2), rep
 
 
+def test_graph_capture_of_cu_limited_call(twn):
+    """A CU-limited call (event join to the 8-CU stream) captured in a HIP
+    graph replays with the whole-chip result's bits.  The replay is not
+    confined to the 8 CUs: graph nodes carry no CU mask."""
+    import torch
+    _say("[graph] CU-limited call captured and replayed")
+    inp = workloads.make_random(8, 300, 8192, "bf16", seed=23)
+    parts, res, wt = inputs_to_dev(inp)
+    ref_out, ref_res = twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"])
+    out = torch.empty_like(res)
+    rout = torch.empty_like(res)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the graph (creates the masked stream)
+        twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=out, residual_out=rout,
+                                 n_cu_limit=8)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        twn.fused_reduce_rmsnorm(parts, res, wt, inp["eps"], out=out, residual_out=rout,
+                                 n_cu_limit=8)
+    for rep in range(3):
+        out.fill_(-1.0)
+        rout.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(rout, ref_res), rep
+    _assert_rows(inp, from_dev(out, "bf16"), from_dev(rout, "bf16"), "graph replay on 8 CUs")
+
+
 @pytest.mark.parametrize("n", list(range(1, 17)))
 def test_every_partial_count(twn, n):
     """Each partial count is its own kernel instantiation: run every one of
