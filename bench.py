@@ -17,7 +17,8 @@ pair on the headline's buffers.  --report PATH also writes a detailed JSON: the
 unfused pair, the AllGather store, decode-size rows, the two-split overlap
 beside a GEMM, row-count scaling, the plain-copy
 ceiling, the ceiling of the fused call's own traffic pattern, the same step
-as plain eager PyTorch ops, and a cache-resident figure.
+as plain eager PyTorch ops, the isolated single call's time, and a
+cache-resident figure.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
 """
@@ -233,6 +234,32 @@ def time_steps(step_fns, steps, warmup, stream=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, wall
+
+
+def time_single_calls(step_fns, calls=60, stream=None):
+    """One call at a time between two events, behind the gate delay, with a
+    device synchronisation after each: the isolated call's time (no
+    neighbour to overlap its start or end), over `calls` calls of the
+    rotating sets.  Returns the median, p10 and p90 in microseconds."""
+    import torch
+    n = len(step_fns)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    for f in step_fns:
+        f()
+    torch.cuda.synchronize()
+    per_call = []
+    for i in range(calls):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        gate(s)
+        a.record(s)
+        step_fns[i % n]()
+        b.record(s)
+        torch.cuda.synchronize()
+        per_call.append(a.elapsed_time(b) * 1e3)
+    d = batch_distribution(per_call, 1)
+    return {"calls": calls, "median_us": d["median_us"], "p10_us": d["p10_us"],
+            "p90_us": d["p90_us"]}
 
 
 # ---------------------------------------------------------------------------
@@ -786,6 +813,10 @@ def main(argv=None):
         tms = measure_torch_eager(w, sets, max(20, args.steps // 10), 5)
         rep["torch_eager_same_step"] = {"ms": tms, "gbs_on_fused_bytes": bytes_call / (tms * 1e-3) / 1e9,
                                         "fused_speedup": tms / ms}
+        fns = [twn.PreparedFused(d["parts"], d["res"], d["w"], w.eps, d["out"], d["res_out"],
+                                 n_cu_limit=args.cu, stream=masked) for d in sets]
+        rep["single_call"] = time_single_calls(fns, stream=masked)
+        del fns
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
