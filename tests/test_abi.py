@@ -257,7 +257,13 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 12288, 8) == (4, 6, 0)
     assert twn.query_fused_shape(BF16, 5120, 4) == (4, 3, 0)     # default rule: 4 waves
     assert twn.query_fused_shape(BF16, 5120, 2) == (5, 2, 0)
-    assert twn.query_fused_shape(BF16, 2048, 2) == (4, 1, 0)     # 4 waves, fewest slots
+    assert twn.query_fused_shape(BF16, 2048, 2) == (1, 4, 0)     # <= 256 chunks: one wave per row
+    assert twn.query_fused_shape(BF16, 512, 8) == (1, 1, 0)
+    assert twn.query_fused_shape(F32, 256, 2) == (1, 1, 0)
+    assert twn.query_fused_shape(BF16, 768, 2) == (1, 2, 0)
+    assert twn.query_fused_shape(BF16, 1536, 16) == (1, 3, 0)
+    assert twn.query_fused_shape(F32, 1024, 8) == (1, 4, 0)
+    assert twn.query_fused_shape(BF16, 3072, 8) == (4, 2, 0)     # 384 chunks: 4 waves, fewest slots
     w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
     w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8, 2)   # the widest row
@@ -272,7 +278,7 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 8192, 8, rows=2048, cus=129) == (4, 4, 0)
     assert twn.query_fused_shape(BF16, 5120, 4, rows=4096, cus=32) == (10, 1, 0)
     assert twn.query_fused_shape(BF16, 4096, 2, rows=4096, cus=32) == (2, 4, 0)
-    assert twn.query_fused_shape(BF16, 2048, 2, rows=4096, cus=32) == (4, 1, 0)   # none measured
+    assert twn.query_fused_shape(BF16, 2048, 2, rows=4096, cus=32) == (1, 4, 0)   # none measured
     assert twn.query_fused_shape(BF16, 8192, 8, rows=64, cus=8, device_cus=8) == (4, 4, 0)
     assert twn.query_fused_shape(BF16, 5120, 4, rows=8, cus=256) == (10, 1, 0)
     assert twn.query_fused_shape(BF16, 4096, 2, rows=8, cus=256) == (8, 1, 0)
