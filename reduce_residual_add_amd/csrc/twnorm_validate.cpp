@@ -288,6 +288,15 @@ static const TunedShape kTuned[] = {
     {2, 1536, 1, 3, 12, 2},  // 12288 bf16 features, few partials
     {2, 2048, 1, 1, 16, 2},  // 16384 bf16 features, one partial (+10% over 4 x 8)
     {2, 2048, 2, 2, 8, 4},   // 16384 bf16 features, two partials (+4% over 4 x 8)
+    // 2560-3584 bf16 features: each entry gained over the 4 x 2 default at
+    // both 1024 and 4096 rows; partial counts where no shape did keep it
+    {2, 320, 2, 5, 5, 1},    // 2560 bf16, 2-5 partials: every lane busy (+0.2-3.5%)
+    {2, 320, 8, 8, 5, 1},    // 2560 bf16, 8 partials (+0.3-1.6%)
+    {2, 384, 2, 2, 3, 2},    // 3072 bf16, 2 partials (+0.3-1.3%)
+    {2, 384, 3, 4, 6, 1},    // 3072 bf16, 3-4 partials (+0.2-2.9%)
+    {2, 384, 8, 16, 1, 6},   // 3072 bf16, 8-16 partials: one wave per row (+2.7-5.8%)
+    {2, 448, 3, 4, 7, 1},    // 3584 bf16, 3-4 partials (+0.3-2.9%)
+    {2, 448, 8, 16, 1, 8},   // 3584 bf16, 8-16 partials: one wave per row (+1.3-8.4%)
 };
 
 // Shapes measured fastest when a call runs on at most half of the CUs: on 8,

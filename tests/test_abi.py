@@ -263,7 +263,13 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 768, 2) == (1, 2, 0)
     assert twn.query_fused_shape(BF16, 1536, 16) == (1, 3, 0)
     assert twn.query_fused_shape(F32, 1024, 8) == (1, 4, 0)
-    assert twn.query_fused_shape(BF16, 3072, 8) == (4, 2, 0)     # 384 chunks: 4 waves, fewest slots
+    assert twn.query_fused_shape(BF16, 3072, 8) == (1, 6, 0)     # measured mid widths
+    assert twn.query_fused_shape(BF16, 3072, 6) == (4, 2, 0)     # 384 chunks: 4 waves, fewest slots
+    assert twn.query_fused_shape(BF16, 3072, 4) == (6, 1, 0)
+    assert twn.query_fused_shape(BF16, 2560, 8) == (5, 1, 0)
+    assert twn.query_fused_shape(BF16, 2560, 12) == (4, 2, 0)
+    assert twn.query_fused_shape(BF16, 3584, 16) == (1, 8, 0)
+    assert twn.query_fused_shape(BF16, 3584, 5) == (4, 2, 0)
     w, k, t = twn.query_fused_shape(BF16, 5120, 4)
     assert t == 0 and w * 64 * k >= 640
     w, k, t = twn.query_fused_shape(BF16, 16 * 64 * 8 * 8, 2)   # the widest row
