@@ -693,6 +693,8 @@ INVARIANCE_CASES = [
     (2, 7, 4096, "f32"),      # 1024 chunks of fp32
     (3, 9, 200, "bf16"),      # 25 chunks: the narrow-row kernel by default
     (2, 3, 1000, "f32"),      # 250 chunks, ragged last group
+    (2, 6, 296, "bf16"),      # 37 chunks: one wave per row, one ragged group
+    (8, 3, 3072, "bf16"),     # 384 chunks: a measured one-wave shape (1 x 6)
 ]
 
 
