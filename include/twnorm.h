@@ -30,6 +30,11 @@
  *   Memory     All data pointers are device pointers owned by the caller.  The
  *              library never allocates, frees or keeps them after returning.
  *              The host array `partials` is read during the call only.
+ *   Device     The pointers and `stream` belong to the current HIP device
+ *              (hipGetDevice), whose CU count and CU-masked streams the call
+ *              uses.  This is not checked (it would cost a runtime query per
+ *              pointer): memory of another device is then accessed from this
+ *              one.  The Python binding checks it.
  *   Execution  Asynchronous: work is enqueued on `stream` (a hipStream_t
  *              passed as an opaque pointer; NULL = the null stream) and the
  *              call returns.  No device synchronisation, no allocation.

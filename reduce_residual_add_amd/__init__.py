@@ -182,13 +182,32 @@ def _stream_ptr(stream=None) -> int:
     return int(torch.cuda.current_stream().cuda_stream)
 
 
+def _stream_device_index(stream):
+    """Device index of a torch stream object, or None if it does not say."""
+    sdev = getattr(stream, "device", None)
+    return None if sdev is None else sdev.index
+
+
+def _check_device(index: int, stream=None) -> None:
+    """The tensors' device `index` and `stream`'s device must be the current
+    device: the library launches there and takes its CU count from it."""
+    cur = _torch()._C._cuda_getDevice()
+    if index != cur:
+        raise ValueError(f"the tensors are on cuda:{index} but the current device is cuda:{cur}; "
+                         f"call inside torch.cuda.device({index})")
+    if stream is not None:
+        sidx = _stream_device_index(stream)
+        if sidx is not None and sidx != cur:
+            raise ValueError(f"the stream is on cuda:{sidx} but the current device is cuda:{cur}")
+
+
 def _rows_hidden(t):
     if t.dim() != 2:
         raise ValueError("tensors are [rows, hidden]")
     return int(t.shape[0]), int(t.shape[1])
 
 
-def _check_fused_tensors(partials, residual, weight, out, residual_out):
+def _check_fused_tensors(partials, residual, weight, out, residual_out, stream=None):
     """Device, dtype, shape and contiguity of a fused call's tensors; returns
     (rows, hidden, n).  One combined test per tensor on the common path; the
     per-property checks below run only to word the error."""
@@ -197,9 +216,11 @@ def _check_fused_tensors(partials, residual, weight, out, residual_out):
     if len(shape) == 2 and residual.is_cuda and 1 <= n <= TW_MAX_PARTIALS:
         dt, dev = residual.dtype, residual.get_device()
         wshape = shape[1:]
-        ok = residual.is_contiguous() and (
-            weight.is_cuda and weight.dtype is dt and weight.get_device() == dev and
-            weight.shape == wshape and weight.is_contiguous())
+        ok = (dev == _torch()._C._cuda_getDevice() and
+              (stream is None or _stream_device_index(stream) in (None, dev)) and
+              residual.is_contiguous() and
+              weight.is_cuda and weight.dtype is dt and weight.get_device() == dev and
+              weight.shape == wshape and weight.is_contiguous())
         if ok:
             for t in (out, residual_out, *partials):
                 if not (t.is_cuda and t.dtype is dt and t.get_device() == dev and t.shape == shape
@@ -208,10 +229,10 @@ def _check_fused_tensors(partials, residual, weight, out, residual_out):
                     break
         if ok:
             return int(shape[0]), int(shape[1]), n
-    return _check_fused_tensors_slow(partials, residual, weight, out, residual_out)
+    return _check_fused_tensors_slow(partials, residual, weight, out, residual_out, stream)
 
 
-def _check_fused_tensors_slow(partials, residual, weight, out, residual_out):
+def _check_fused_tensors_slow(partials, residual, weight, out, residual_out, stream=None):
     rows, hidden = _rows_hidden(residual)
     dt, dev = residual.dtype, residual.device
     n = len(partials)
@@ -223,6 +244,7 @@ def _check_fused_tensors_slow(partials, residual, weight, out, residual_out):
     _check_tensor(weight, "weight", (hidden,), dt, dev)
     _check_tensor(out, "out", (rows, hidden), dt, dev)
     _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    _check_device(dev.index, stream)
     return rows, hidden, n
 
 
@@ -252,7 +274,7 @@ def fused_reduce_rmsnorm(partials: Sequence, residual, weight, eps: float, *, ou
         out = torch.empty_like(residual)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
-    rows, hidden, n = _check_fused_tensors(partials, residual, weight, out, residual_out)
+    rows, hidden, n = _check_fused_tensors(partials, residual, weight, out, residual_out, stream)
     if rows == 0:   # nothing to do (an empty tensor's data_ptr() may be NULL)
         return out, residual_out
     arr = (_vp * n)(*[p.data_ptr() for p in partials])
@@ -286,6 +308,7 @@ def fused_reduce_rmsnorm_allgather(partials: Sequence, residual, weight, eps: fl
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    _check_device(dev.index, stream)
     if rows == 0:
         return residual_out
     arr = (_vp * n)(*[p.data_ptr() for p in partials])
@@ -312,6 +335,7 @@ def reduce(partials: Sequence, *, out=None, n_cu_limit: int = 0, stream=None):
     if out is None:
         out = torch.empty_like(partials[0])
     _check_tensor(out, "out", (rows, hidden), dt, dev)
+    _check_device(dev.index, stream)
     if rows == 0:
         return out
     arr = (_vp * n)(*[p.data_ptr() for p in partials])
@@ -337,6 +361,7 @@ def rmsnorm(reduced, residual, weight, eps: float, *, out=None, residual_out=Non
         residual_out = torch.empty_like(residual)
     _check_tensor(out, "out", (rows, hidden), dt, dev)
     _check_tensor(residual_out, "residual_out", (rows, hidden), dt, dev)
+    _check_device(dev.index, stream)
     if rows == 0:
         return out, residual_out
     _check(lib.tw_rmsnorm(reduced.data_ptr(), rows, hidden, dtype_code(residual),
@@ -363,6 +388,7 @@ def stream_copy(src, dst, *, n_cu_limit: int = 0, stream=None):
     lib = load()
     nbytes = src.numel() * src.element_size()
     _check_raw((src, dst), ("src", "dst"), nbytes, src.device)
+    _check_device(src.device.index, stream)
     _check(lib.tw_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, int(n_cu_limit),
                               _stream_ptr(stream)))
     return dst
@@ -379,6 +405,7 @@ def stream_mix(srcs: Sequence, dsts: Sequence, *, n_cu_limit: int = 0, stream=No
     nbytes = srcs[0].numel() * srcs[0].element_size()
     _check_raw(list(srcs) + list(dsts), [f"srcs[{i}]" for i in range(n_src)] +
                [f"dsts[{j}]" for j in range(n_dst)], nbytes, srcs[0].device)
+    _check_device(srcs[0].device.index, stream)
     if nbytes == 0:
         return dsts
     sa = (_vp * n_src)(*[t.data_ptr() for t in srcs])
@@ -442,7 +469,8 @@ class PreparedFused:
     def __init__(self, partials, residual, weight, eps, out, residual_out, n_cu_limit=0,
                  stream=None):
         self._lib = load()
-        rows, hidden, self._n = _check_fused_tensors(partials, residual, weight, out, residual_out)
+        rows, hidden, self._n = _check_fused_tensors(partials, residual, weight, out, residual_out,
+                                                     stream)
         self._rows = rows
         self._keep = (list(partials), residual, weight, out, residual_out)
         self._arr = (_vp * self._n)(*[p.data_ptr() for p in partials])

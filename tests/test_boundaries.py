@@ -98,3 +98,22 @@ def test_host_tensors_are_refused():
         twn.stream_copy(res, torch.empty_like(res))
     with pytest.raises((ValueError, ImportError)):
         twn.stream_mix([res], [torch.empty_like(res)])
+
+
+def test_tensors_off_the_current_device_are_refused(monkeypatch):
+    """The library launches on the current device and takes its CU count
+    from it, so the binding refuses tensors or a stream on another device
+    (checked here with a stand-in for torch's current-device query)."""
+    import types
+    import reduce_residual_add_amd as twn
+    fake = types.SimpleNamespace(_C=types.SimpleNamespace(_cuda_getDevice=lambda: 0))
+    monkeypatch.setattr(twn, "_torch", lambda: fake)
+    twn._check_device(0)
+    with pytest.raises(ValueError, match="current device is cuda:0"):
+        twn._check_device(1)
+    on1 = types.SimpleNamespace(device=types.SimpleNamespace(index=1))
+    on0 = types.SimpleNamespace(device=types.SimpleNamespace(index=0))
+    twn._check_device(0, on0)
+    twn._check_device(0, object())      # a stream object that names no device
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        twn._check_device(0, on1)
