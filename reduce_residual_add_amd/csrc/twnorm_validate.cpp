@@ -303,10 +303,13 @@ static const TunedShape kTuned[] = {
 // 16, 32 and 64 CUs, 8 x 2 beats the whole-chip 4 x 4 by 4-6% on 8192-wide
 // rows with 8 partials; on 8 and 32 CUs, 10 x 1 beats 8 x 2 by 15-20% on
 // 5120-wide rows with 4 partials (every lane busy, three rows in flight per
-// CU); 2 x 4 beats 8 x 1 by 3-5% on 4096-wide rows with 2 partials.
+// CU) and the whole-chip 4 x 3 by 1-14% with 8-16 partials; 7 x 2 beats the
+// whole-chip 4 x 4 by 1-10% on 7168-wide rows with 4-12 partials (not 16);
+// 2 x 4 beats 8 x 1 by 3-5% on 4096-wide rows with 2 partials.
 static const TunedShape kTunedLimited[] = {
     {2, 1024, 5, 16, 8, 2},
-    {2, 640, 3, 6, 10, 1},
+    {2, 640, 3, 16, 10, 1},
+    {2, 896, 4, 12, 7, 2},
     {2, 512, 1, 3, 2, 4},
 };
 
