@@ -65,7 +65,8 @@
  *              TW_ERR_UNSUPPORTED with a CU limit.  Under HIP-graph capture
  *              a CU-limited call is captured with its event join and replays
  *              with the same results, but a graph node carries no CU mask:
- *              in replay its grid (sized for k CUs) is not confined to them.
+ *              replayed on another stream, its grid (sized for k CUs) is not
+ *              confined to them; replayed on tw_cu_masked_stream(k), it is.
  *              Each distinct CU mask needs a hardware queue of its own until
  *              tw_shutdown(): at most 3 distinct masks (limits k, and
  *              complements from tw_cu_complement_stream) per device and

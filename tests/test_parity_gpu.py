@@ -576,8 +576,9 @@ def test_graph_capture_replays(twn):
 
 def test_graph_capture_of_cu_limited_call(twn):
     """A CU-limited call (event join to the 8-CU stream) captured in a HIP
-    graph replays with the whole-chip result's bits.  The replay is not
-    confined to the 8 CUs: graph nodes carry no CU mask."""
+    graph replays with the whole-chip result's bits, on the capturing stream
+    (not confined to the 8 CUs: graph nodes carry no CU mask) and on the
+    masked stream itself (confined to them)."""
     import torch
     _say("[graph] CU-limited call captured and replayed")
     inp = workloads.make_random(8, 300, 8192, "bf16", seed=23)
@@ -603,6 +604,16 @@ def test_graph_capture_of_cu_limited_call(twn):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(rout, ref_res), rep
+    # replayed on the masked stream itself, where the CU limit holds
+    masked = twn.cu_masked_stream(8)
+    for rep in range(2):
+        out.fill_(-1.0)
+        rout.fill_(-1.0)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(masked):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(rout, ref_res), ("masked", rep)
     _assert_rows(inp, from_dev(out, "bf16"), from_dev(rout, "bf16"), "graph replay on 8 CUs")
 
 
