@@ -17,8 +17,8 @@ pair on the headline's buffers.  --report PATH also writes a detailed JSON: the
 unfused pair, the AllGather store, decode-size rows, the two-split overlap
 beside a GEMM, row-count scaling, the plain-copy
 ceiling, the ceiling of the fused call's own traffic pattern, the same step
-as plain eager PyTorch ops, the isolated single call's time, and a
-cache-resident figure.
+as plain eager PyTorch ops, the isolated single call's time, the oracle
+on every host core, and a cache-resident figure.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--report PATH]
 """
@@ -318,6 +318,39 @@ def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
         "parity_fails": f_out + f_res,
         "parity_max_abs": max(m_out, m_res),
     }
+
+
+def cpu_oracle_threads(inp, w, threads, target_seconds=5.0):
+    """The same oracle on `threads` host threads, each working through its own
+    64-row slices of the inputs (numpy releases the GIL inside its array
+    loops): the all-core host figure beside the single-thread baseline."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import twnorm_oracle as O
+    rows_total = inp["rows"]
+    chunk = min(rows_total, 64)
+    starts = list(range(0, rows_total - chunk + 1, chunk)) or [0]
+
+    def worker(t):
+        done, i = 0, t
+        t_end = time.perf_counter() + target_seconds
+        while time.perf_counter() < t_end:
+            st = starts[i % len(starts)]
+            sl = slice(st, st + chunk)
+            O.fused_from_storage(dict(inp, partials=[p[sl] for p in inp["partials"]],
+                                      residual=inp["residual"][sl]))
+            done += chunk
+            i += threads
+        return done
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        rows = sum(ex.map(worker, range(threads)))
+    wall = time.perf_counter() - t0
+    rows_per_s = rows / wall
+    bytes_per_row = (w.n + 3) * w.hidden * w.elem_bytes
+    return {"threads": threads, "rows": rows, "wall_s": round(wall, 2),
+            "rows_per_s": round(rows_per_s, 1),
+            "gbs": round(rows_per_s * bytes_per_row / 1e9, 4)}
 
 
 def _cpu_model():
@@ -817,6 +850,7 @@ def main(argv=None):
                                  n_cu_limit=args.cu, stream=masked) for d in sets]
         rep["single_call"] = time_single_calls(fns, stream=masked)
         del fns
+        rep["cpu_oracle_threads"] = cpu_oracle_threads(inp, w, len(os.sched_getaffinity(0)))
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
