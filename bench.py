@@ -267,7 +267,12 @@ def time_single_calls(step_fns, calls=60, stream=None):
 # ---------------------------------------------------------------------------
 
 
-def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
+def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds, all_core_threads=0):
+    """The oracle on one host thread over a bounded sample of the inputs
+    (GB/s, rows/s, and its check of the GPU's first rows); with
+    all_core_threads > 0 also the same oracle on that many threads, each
+    working through its own 64-row slices (numpy releases the GIL inside its
+    array loops), as `all_cores`."""
     import numpy as np
     from oracle import twnorm_oracle as O
     rows_total = inp["rows"]
@@ -303,7 +308,31 @@ def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
 
     f_out, m_out = fails(got_out, ref_out)
     f_res, m_res = fails(got_res, ref_res)
-    return {
+    all_cores = None
+    if all_core_threads > 0:
+        from concurrent.futures import ThreadPoolExecutor
+        starts = list(range(0, rows_total - chunk + 1, chunk)) or [0]
+
+        def worker(t):
+            done, i = 0, t
+            t_end = time.perf_counter() + min(target_seconds, 5.0)
+            while time.perf_counter() < t_end:
+                st = starts[i % len(starts)]
+                s2 = slice(st, st + chunk)
+                O.fused_from_storage(dict(inp, partials=[p[s2] for p in inp["partials"]],
+                                          residual=inp["residual"][s2]))
+                done += chunk
+                i += all_core_threads
+            return done
+
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=all_core_threads) as ex:
+            rows_mt = sum(ex.map(worker, range(all_core_threads)))
+        wall = time.perf_counter() - t0
+        all_cores = {"threads": all_core_threads, "rows": rows_mt, "wall_s": round(wall, 2),
+                     "rows_per_s": round(rows_mt / wall, 1),
+                     "value": round(rows_mt / wall * bytes_per_row / 1e9, 4), "unit": "GB/s"}
+    result = {
         "value": round(rows_per_s * bytes_per_row / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
@@ -318,39 +347,9 @@ def cpu_baseline(inp, w, gpu_out, gpu_res_out, target_seconds):
         "parity_fails": f_out + f_res,
         "parity_max_abs": max(m_out, m_res),
     }
-
-
-def cpu_oracle_threads(inp, w, threads, target_seconds=5.0):
-    """The same oracle on `threads` host threads, each working through its own
-    64-row slices of the inputs (numpy releases the GIL inside its array
-    loops): the all-core host figure beside the single-thread baseline."""
-    from concurrent.futures import ThreadPoolExecutor
-    from oracle import twnorm_oracle as O
-    rows_total = inp["rows"]
-    chunk = min(rows_total, 64)
-    starts = list(range(0, rows_total - chunk + 1, chunk)) or [0]
-
-    def worker(t):
-        done, i = 0, t
-        t_end = time.perf_counter() + target_seconds
-        while time.perf_counter() < t_end:
-            st = starts[i % len(starts)]
-            sl = slice(st, st + chunk)
-            O.fused_from_storage(dict(inp, partials=[p[sl] for p in inp["partials"]],
-                                      residual=inp["residual"][sl]))
-            done += chunk
-            i += threads
-        return done
-
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        rows = sum(ex.map(worker, range(threads)))
-    wall = time.perf_counter() - t0
-    rows_per_s = rows / wall
-    bytes_per_row = (w.n + 3) * w.hidden * w.elem_bytes
-    return {"threads": threads, "rows": rows, "wall_s": round(wall, 2),
-            "rows_per_s": round(rows_per_s, 1),
-            "gbs": round(rows_per_s * bytes_per_row / 1e9, 4)}
+    if all_cores is not None:
+        result["all_cores"] = all_cores
+    return result
 
 
 def _cpu_model():
@@ -791,7 +790,8 @@ def main(argv=None):
                                  residual_out=d0["res_out"])
         torch.cuda.synchronize()
         result["cpu_baseline"] = cpu_baseline(inp, w, _from_dev(d0["out"], w.dtype),
-                                              _from_dev(d0["res_out"], w.dtype), args.cpu_seconds)
+                                              _from_dev(d0["res_out"], w.dtype), args.cpu_seconds,
+                                              len(os.sched_getaffinity(0)) if args.report else 0)
 
     if not args.no_per_config:
         result["per_config"] = measure_per_config(twn, args, w, sets, ms, dev_cus)
@@ -850,7 +850,6 @@ def main(argv=None):
                                  n_cu_limit=args.cu, stream=masked) for d in sets]
         rep["single_call"] = time_single_calls(fns, stream=masked)
         del fns
-        rep["cpu_oracle_threads"] = cpu_oracle_threads(inp, w, len(os.sched_getaffinity(0)))
         # cache-resident figure (one buffer set, repeated): NOT an HBM number
         wms, _ = measure_fused(twn, w, sets[:1], args.cu, 200, 20)
         rep["warm_same_buffers_not_hbm"] = {"ms": wms, "gbs": bytes_call / (wms * 1e-3) / 1e9}
