@@ -1,6 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
 the same seeded inputs.  Needs an MI355X; every case prints what it runs
 before touching the GPU."""
+import os
 import sys
 
 import numpy as np
@@ -821,31 +822,48 @@ def test_concurrent_host_threads(twn):
 # multiple of 16 bytes up to the widest row), row count and in-place use,
 # each checked element by element against the oracle.
 # ---------------------------------------------------------------------------
-def _random_configs(count=120, seed=2024):
+def _random_configs(count, seed, rows_lo, rows_hi, wide_top=2048, cu_choices=(0,)):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(count):
         dtype = "bf16" if rng.random() < 0.75 else "f32"
         per_chunk = 8 if dtype == "bf16" else 4
         max_chunks = (64 * 1024 if dtype == "bf16" else 32 * 1024) // per_chunk
-        # widths spread over every scale: mostly up to 2048 chunks, some wider
-        top = max_chunks if rng.random() < 0.15 else 2048
-        chunks = int(np.exp(rng.uniform(0, np.log(top))))
-        out.append((int(rng.integers(1, 17)), int(rng.integers(1, 49)),
-                    max(1, chunks) * per_chunk, dtype, bool(rng.random() < 0.3)))
+        # widths spread over every scale: mostly up to wide_top chunks, some wider
+        top = max_chunks if rng.random() < 0.15 else wide_top
+        chunks = max(1, int(np.exp(rng.uniform(0, np.log(top)))))
+        cu = int(rng.choice(cu_choices))
+        if chunks > 10 * 64 * 8:   # wider than a CU-limited call's workgroups take
+            cu = 0
+        out.append((int(rng.integers(1, 17)), int(rng.integers(rows_lo, rows_hi + 1)),
+                    chunks * per_chunk, dtype, bool(rng.random() < 0.3), cu))
     return out
 
 
-RANDOM_CASES = _random_configs()
+# TW_RANDOM_SCALE=k multiplies both sweeps' case counts (one-off extended runs)
+_SCALE = max(1, int(os.environ.get("TW_RANDOM_SCALE", "1")))
+# decode-sized calls (fewer rows than CUs) on the whole chip
+RANDOM_CASES = _random_configs(120 * _SCALE, 2024, 1, 48)
+# calls of several hundred rows, on the whole chip or on 8 or 32 CUs
+RANDOM_WIDE_CASES = _random_configs(24 * _SCALE, 4048, 256, 700, wide_top=1536,
+                                    cu_choices=(0, 0, 8, 32))
+
+
+def _run_random_cases(twn, cases, seed0, label):
+    _say(f"[{label}] {len(cases)} cases")
+    for i, (n, rows, hidden, dtype, in_place, cu) in enumerate(cases):
+        _say(f"  case {i}: n={n} rows={rows} H={hidden} {dtype} in_place={in_place} cu={cu}")
+        inp = workloads.make_random(n, rows, hidden, dtype, seed=seed0 + i)
+        out, res_out = _run_fused(twn, inp, n_cu_limit=cu, in_place=in_place)
+        _assert_rows(inp, out, res_out, f"{label} case {i}")
 
 
 def test_fused_random_configs(twn):
-    _say(f"[random configs] {len(RANDOM_CASES)} cases")
-    for i, (n, rows, hidden, dtype, in_place) in enumerate(RANDOM_CASES):
-        _say(f"  case {i}: n={n} rows={rows} H={hidden} {dtype} in_place={in_place}")
-        inp = workloads.make_random(n, rows, hidden, dtype, seed=10_000 + i)
-        out, res_out = _run_fused(twn, inp, in_place=in_place)
-        _assert_rows(inp, out, res_out, f"case {i}")
+    _run_random_cases(twn, RANDOM_CASES, 10_000, "random configs")
+
+
+def test_fused_random_configs_many_rows(twn):
+    _run_random_cases(twn, RANDOM_WIDE_CASES, 20_000, "random configs, many rows")
 
 
 # ---------------------------------------------------------------------------
