@@ -305,12 +305,16 @@ static const TunedShape kTuned[] = {
 // 5120-wide rows with 4 partials (every lane busy, three rows in flight per
 // CU) and the whole-chip 4 x 3 by 1-14% with 8-16 partials; 7 x 2 beats the
 // whole-chip 4 x 4 by 1-10% on 7168-wide rows with 4-12 partials (not 16);
-// 2 x 4 beats 8 x 1 by 3-5% on 4096-wide rows with 2 partials.
+// 8 x 3 beats the whole-chip default 4 x 6 by 1-7% on 12288-wide rows with
+// 1-4 partials (not 8; the whole-chip 12 x 2 exceeds the limited calls'
+// workgroups); 2 x 4 beats 8 x 1 by 3-5% on 4096-wide rows with 2 partials
+// and by 1-2% with 4.
 static const TunedShape kTunedLimited[] = {
     {2, 1024, 5, 16, 8, 2},
     {2, 640, 3, 16, 10, 1},
     {2, 896, 4, 12, 7, 2},
-    {2, 512, 1, 3, 2, 4},
+    {2, 1536, 1, 4, 8, 3},
+    {2, 512, 1, 4, 2, 4},
 };
 
 // The whole-chip shape of a wide row:

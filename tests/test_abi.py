@@ -287,6 +287,10 @@ def test_shape_choice(lib):
     assert twn.query_fused_shape(BF16, 7168, 8, rows=2048, cus=32) == (7, 2, 0)
     assert twn.query_fused_shape(BF16, 7168, 16, rows=2048, cus=32) == (4, 4, 0)
     assert twn.query_fused_shape(BF16, 7168, 8, rows=2048, cus=256) == (4, 4, 0)
+    assert twn.query_fused_shape(BF16, 12288, 3, rows=2048, cus=8) == (8, 3, 0)
+    assert twn.query_fused_shape(BF16, 12288, 8, rows=2048, cus=8) == (4, 6, 0)
+    assert twn.query_fused_shape(BF16, 4096, 4, rows=2048, cus=32) == (2, 4, 0)
+    assert twn.query_fused_shape(BF16, 4096, 5, rows=2048, cus=32) == (8, 1, 0)
     assert twn.query_fused_shape(BF16, 4096, 2, rows=4096, cus=32) == (2, 4, 0)
     assert twn.query_fused_shape(BF16, 2048, 2, rows=4096, cus=32) == (1, 4, 0)   # none measured
     assert twn.query_fused_shape(BF16, 8192, 8, rows=64, cus=8, device_cus=8) == (4, 4, 0)
