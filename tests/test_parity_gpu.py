@@ -313,6 +313,34 @@ def test_special_values(twn):
         assert tolerance_report(from_dev(out, dt)[3:4], ref, dt)["fails"] == 0
 
 
+def test_subnormal_inputs(twn):
+    """bf16 subnormal residuals and partials are neither flushed nor
+    rounded: float32 holds every bf16 subnormal and the sum of two of them
+    exactly, so residual_out equals the oracle's value bit for bit; out is
+    checked to the usual bar.  Whole chip and 8 CUs."""
+    _say("[edge] subnormal inputs")
+    rows, h = 6, 8192
+    rng = np.random.default_rng(11)
+
+    def subnormal_bits(hi):
+        bits = rng.integers(1, hi, size=(rows, h)).astype(np.uint16)
+        return bits | (rng.integers(0, 2, size=(rows, h)).astype(np.uint16) << 15)
+
+    r = subnormal_bits(128)
+    r[:, :8] = 0x3F80                       # a few ones, so no row's mean square is tiny
+    p0 = subnormal_bits(64)
+    p1 = np.zeros((rows, h), np.uint16)      # adding a zero partial is exact too
+    p0[1] = 0                                # row 1: the residual alone
+    inp = dict(partials=[p0, p1], residual=r, weight=np.full(h, 0x3F80, np.uint16), eps=1e-5,
+               dtype="bf16", n=2, rows=rows, hidden=h)
+    ref_out, ref_res = O.fused_from_storage(inp)
+    for cu in (0, 8):
+        out, res_out = _run_fused(twn, inp, n_cu_limit=cu)
+        assert np.array_equal(res_out, O.bf16_encode_rne(ref_res)), f"residual_out at cu {cu}"
+        assert np.array_equal(res_out[1], r[1])
+        _assert_rows(inp, out, res_out, f"subnormal inputs cu{cu}")
+
+
 def test_fourth_cu_limit_is_refused(twn):
     """A fourth distinct CU limit in one process is refused with a clear
     error before anything is enqueued (each limit holds a hardware queue)."""
